@@ -1,0 +1,397 @@
+#!/usr/bin/env python3
+"""Throughput of the direct sequence<->head relayout on one MI355X.
+
+Workload: the representative 55,413-token shape of the Vflash "Sol-Engine
+alignment" page ("What is enabled"): 55,413 tokens padded to 55,414 over
+P = 2 ranks (27,707 tokens each), C = 4 chunks, H = 56 heads of 128, BF16,
+synthetic N(0,1) values (seed 1, one stream per rank).
+
+A step is one pass of the relayout path for every rank, inputs resident in
+HBM: QKV pack, QKV unpack, attention-result split and returned-head merge,
+each launched through the C ABI.  The exchanges between them are the
+collective's job (RCCL over xGMI on a real multi-GPU run), not the path's;
+they run once before timing to fill the receive buffers and are not timed.
+
+Printed: one JSON line with the whole step's effective HBM throughput
+(algorithmic bytes: every element read once and written once), per-op
+times from HIP events recorded on the launch stream, the roofline of the
+dominant kernel (QKV pack) against the 8 TB/s HBM3E peak, a device-to-device
+copy of the pack's size for comparison, and the CPU oracle timed on the
+host's cores on a bounded sample (rank 0's four chains once).
+
+Other modes: --mode pmc runs only QKV pack (rank 0) and a plain torch copy
+kernel of known size, for rocprofv3 counter runs; --pmc-summary turns the
+counter CSVs of those runs into the traffic figures kept under profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QKV-pack / head-merge ms and effective HBM GB/s (% of peak) at 55,413 tokens"
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_pack_repr55413_traffic.txt")
+KERNEL_SOURCES = ["head_relayout_amd/csrc/vrl_kernels.hip", "head_relayout_amd/csrc/vrl_internal.h",
+                  "head_relayout_amd/csrc/vrl_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def say(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (3 = the representative shape)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    ap.add_argument("--reps", type=int, default=10, help="launches per kernel in --mode pmc")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc output trees (FETCH_SIZE, WRITE_SIZE)")
+    return ap.parse_args()
+
+
+# ---- device-side setup ---------------------------------------------------------
+
+class Rank:
+    """One virtual rank's buffers, all resident in HBM."""
+
+    def __init__(self, w, r, dev, torch, np, datagen, vrl):
+        P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+        self.host = datagen.fused_source(w, r)
+        self.fused = torch.from_numpy(self.host.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.qkv = [self.fused[:, i * H * D:(i + 1) * H * D].unflatten(1, (H, D)) for i in range(3)]
+        n_qkv = vrl.exchange_elems(vrl.VRL_EXCHANGE_QKV, P, C, S_l, H, D)
+        n_att = vrl.exchange_elems(vrl.VRL_EXCHANGE_ATTN, P, C, S_l, H, D)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.packed = torch.empty(n_qkv, **bf)
+        self.recv = torch.empty(n_qkv, **bf)
+        self.planes = [torch.empty(S, G, D, **bf) for _ in range(3)]
+        self.send = torch.empty(n_att, **bf)
+        self.back = torch.empty(n_att, **bf)
+        self.merged = torch.empty(S_l, H, D, **bf)
+
+
+def exchange(srcs, dsts, P):
+    """All-to-all of P ranks' destination-major wire buffers inside one HBM."""
+    for s in range(P):
+        for r in range(P):
+            dsts[r].view(P, -1)[s].copy_(srcs[s].view(P, -1)[r])
+
+
+def op_bytes(w) -> dict:
+    """Algorithmic bytes per launch (each element read once, written once)."""
+    qkv = 2 * 3 * w.s_local * w.H * w.D * 2
+    att = 2 * w.s_local * w.H * w.D * 2
+    return {"qkv_pack": qkv, "qkv_unpack": qkv, "attn_split": att, "head_merge": att}
+
+
+def run_bench(args):
+    import numpy as np
+    import torch
+
+    import datagen
+    import head_relayout_amd as vrl
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    w = datagen.WORKLOADS[args.workload]
+    P, C = w.P, w.C
+    say(f"[bench] workload {w.cid} ({w.name}): generating inputs for {P} ranks")
+    ranks = [Rank(w, r, dev, torch, np, datagen, vrl) for r in range(P)]
+    torch.cuda.synchronize()
+
+    def pack(rk):
+        vrl.qkv_pack(*rk.qkv, rk.packed, P, C)
+
+    def unpack(rk):
+        vrl.qkv_unpack(rk.recv, *rk.planes, P, C)
+
+    def split(rk):
+        vrl.attn_split(rk.planes[0], rk.send, P, C)
+
+    def merge(rk):
+        vrl.head_merge(rk.back, rk.merged, P, C)
+
+    # One full pass with the exchanges, to fill every receive buffer.
+    for rk in ranks:
+        pack(rk)
+    exchange([rk.packed for rk in ranks], [rk.recv for rk in ranks], P)
+    for rk in ranks:
+        unpack(rk)
+        split(rk)
+    exchange([rk.send for rk in ranks], [rk.back for rk in ranks], P)
+    for rk in ranks:
+        merge(rk)
+    torch.cuda.synchronize()
+
+    def round_trip_ok() -> bool:
+        # merge(exchange(split(unpack(exchange(pack(x))))[Q])) must be x's Q
+        return all(torch.equal(rk.merged.view(torch.int16), rk.qkv[0].view(torch.int16))
+                   for rk in ranks)
+
+    if not round_trip_ok():
+        raise SystemExit("round trip is not bit-exact")
+
+    ops = [("qkv_pack", pack), ("qkv_unpack", unpack), ("attn_split", split), ("head_merge", merge)]
+    nbytes = op_bytes(w)
+    step_bytes = P * sum(nbytes.values())
+
+    def step(events=None):
+        for name, fn in ops:
+            for rk in ranks:
+                if events is not None:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn(rk)
+                    b.record()
+                    events[name].append((a, b))
+                else:
+                    fn(rk)
+
+    say(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    say(f"[bench] timing {args.steps} steps")
+    events = {name: [] for name, _ in ops}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    per_op = {}
+    for name, _ in ops:
+        times = sorted(a.elapsed_time(b) for a, b in events[name])
+        mean = sum(times) / len(times)
+        gbs = nbytes[name] / (mean * 1e-3) / 1e9
+        per_op[name] = {"ms": round(mean, 5), "ms_median": round(times[len(times) // 2], 5),
+                        "ms_min": round(times[0], 5), "bytes": nbytes[name],
+                        "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                        "launches": len(times)}
+
+    if not round_trip_ok():
+        raise SystemExit("round trip is not bit-exact after timing")
+
+    # A device-to-device copy of the pack's size, for comparison.
+    src = ranks[0].packed
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_ms = a.elapsed_time(b) / 10
+    copy_gbs = 2 * src.numel() * 2 / (copy_ms * 1e-3) / 1e9
+    del dst
+
+    dominant = "qkv_pack"
+    achieved = per_op[dominant]["gbs"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(),
+                "kernel": "qkv_pack (relayout_kernel<Pack, 16 B, contiguous>)",
+                "bytes_per_launch": nbytes[dominant]}
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.total_tokens} tokens padded to {w.S}, P={P} ranks x "
+                               f"{w.s_local} tokens, C={C}, H={w.H}, D={w.D}",
+                   "P": P, "C": C, "s_local": w.s_local, "H": w.H, "D": w.D,
+                   "step": "qkv_pack + qkv_unpack + attn_split + head_merge for each rank",
+                   "bytes_per_step": step_bytes},
+        "ops": per_op,
+        "roofline": roofline,
+        "copy_d2d": {"bytes": 2 * src.numel() * 2, "ms": round(copy_ms, 5), "gbs": round(copy_gbs, 1)},
+        "verified": "round trip bit-exact before and after timing",
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, ranks[0].host, nbytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, host, nbytes):
+    """The oracle's four chains on rank 0's inputs, once each, on the host."""
+    import numpy as np
+
+    import oracle
+
+    d = oracle.dims(w.P, w.C, w.s_local, w.H, w.D)
+    q, k, v = [host[:, i * w.H * w.D:(i + 1) * w.H * w.D].reshape(w.s_local, w.H, w.D)
+               for i in range(3)]
+    packed = np.full(oracle.exchange_elems(d, 0), 0, dtype=np.uint16)
+    planes = [np.full((w.S, w.G, w.D), 0, dtype=np.uint16) for _ in range(3)]
+    send = np.full(oracle.exchange_elems(d, 1), 0, dtype=np.uint16)
+    merged = np.full((w.s_local, w.H, w.D), 0, dtype=np.uint16)
+    say("[bench] cpu baseline: untimed warm-up pass of the pack chain")
+    oracle.qkv_pack(d, q, k, v, packed)
+    say("[bench] cpu baseline: timing the four chains")
+    times = {}
+    t = time.perf_counter()
+    oracle.qkv_pack(d, q, k, v, packed)
+    times["qkv_pack"] = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.qkv_unpack(d, packed, *planes)
+    times["qkv_unpack"] = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.attn_split(d, planes[0], send)
+    times["attn_split"] = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.head_merge(d, send, merged)
+    times["head_merge"] = time.perf_counter() - t
+    total = sum(times.values())
+    return {"value": round(sum(nbytes.values()) / total / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": "rank 0 of 2: the pack, unpack, split and merge chains once each "
+                      "(pack's receive buffer stands in for the exchanged one)",
+            "ms": {k: round(1e3 * v, 1) for k, v in times.items()}}
+
+
+def read_traffic():
+    """HBM bytes per QKV pack launch from the committed counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                fields[parts[0]] = parts[1]
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+# ---- counter runs --------------------------------------------------------------
+
+def run_pmc(args):
+    """QKV pack of rank 0 and a plain copy kernel, `reps` launches each."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import head_relayout_amd as vrl
+
+    dev = torch.device("cuda:0")
+    w = datagen.WORKLOADS[args.workload]
+    rk = Rank(w, 0, dev, torch, np, datagen, vrl)
+    n = rk.packed.numel()
+    a = torch.zeros(n, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(args.reps):
+        vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
+    for _ in range(args.reps):
+        torch.bitwise_not(a, out=b)     # reads n*2 bytes, writes n*2 bytes
+    torch.cuda.synchronize()
+    print(f"pmc: {args.reps} x qkv_pack ({op_bytes(w)['qkv_pack'] // 2} B read + written), "
+          f"{args.reps} x bitwise_not copy kernel ({2 * n} B read + written)", flush=True)
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the pack kernel and of
+    the copy kernel; the copy kernel's known size calibrates the counters."""
+    def load(d, counter):
+        rows = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row["Kernel_Name"]
+                    rows.setdefault(name, []).append(float(row["Counter_Value"]))
+        return rows
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+
+    def pick(rows, key):
+        ks = [k for k in rows if key in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {key!r} in {sorted(rows)}")
+        vals = rows[ks[0]]
+        return ks[0], sum(vals) / len(vals), len(vals)
+
+    import datagen
+    w = datagen.WORKLOADS[3]
+    pack_bytes = op_bytes(w)["qkv_pack"] // 2           # read (= written) bytes per launch
+    copy_bytes = 3 * w.s_local * w.H * w.D * 2
+    kp, pf, npf = pick(fetch, "relayout_kernel")
+    kc, cf, ncf = pick(fetch, "bitwise_not")
+    _, pw, npw = pick(write, "relayout_kernel")
+    _, cw, ncw = pick(write, "bitwise_not")
+    f_scale = copy_bytes / (cf * 1024)
+    w_scale = copy_bytes / (cw * 1024)
+    pack_fetch = pf * 1024 * f_scale
+    pack_write = pw * 1024 * w_scale
+    lines = [
+        f"kernel_source_sha256 {kernel_source_hash()}",
+        f"hbm_bytes_per_launch {int(round(pack_fetch + pack_write))}",
+        f"# pack kernel: {kp}",
+        f"#   FETCH_SIZE {pf:.1f} KiB/dispatch over {npf} dispatches, WRITE_SIZE {pw:.1f} KiB/dispatch over {npw}",
+        f"# copy kernel: {kc}",
+        f"#   FETCH_SIZE {cf:.1f} KiB/dispatch over {ncf}, WRITE_SIZE {cw:.1f} KiB/dispatch over {ncw}",
+        f"#   known size {copy_bytes} B read and {copy_bytes} B written per dispatch",
+        f"#   calibration: fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+        f"# pack per launch: fetched {pack_fetch:.0f} B, written {pack_write:.0f} B;"
+        f" algorithmic {pack_bytes} B each way ({pack_fetch / pack_bytes:.4f}x, {pack_write / pack_bytes:.4f}x)",
+    ]
+    print("\n".join(lines))
+
+
+def main():
+    args = parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the P ranks' "
+              f"buffers and their exchange are modelled inside one GPU's HBM; a multi-GPU run "
+              f"would exchange through RCCL and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "pmc":
+        run_pmc(args)
+    else:
+        run_bench(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,30 @@
+"""Builds libvrl.so for gfx950 with hipcc, in place next to this file."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "vrl_kernels.hip"), os.path.join(CSRC, "vrl_api.cpp")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    # no packed-FP32 instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(out: str | None = None, defines: tuple = ()) -> str:
+    """Compiles the library; `defines` are extra -D macros (build-time tuning
+    knobs such as VRL_UNROLL), `out` an alternative output path."""
+    out = out or os.path.join(HERE, "libvrl.so")
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-o", tmp, *SOURCES]
+    subprocess.check_call(cmd)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,464 @@
+// C ABI of libvrl.so: argument validation, launch planning, kernel launch.
+//
+// Every check runs before anything is enqueued, in this order: dimensions and
+// window (VRL_E_INVALID), pointers and layouts (VRL_E_INVALID / VRL_E_LAYOUT),
+// the launch plan's size limits (VRL_E_INVALID), then the device and the
+// pointers' allocations (VRL_E_DEVICE / VRL_E_INVALID).  All but the last
+// group need no GPU, so they are exercised by the host-only tests.  The fail-closed behaviour (no silent fallback; layouts
+// outside the contract are reported so the caller keeps its materialising
+// path) follows the Vflash "Sol-Engine alignment" page, "What is enabled",
+// and its note on incompatible layouts raising rather than falling back.
+#include "../../include/vrl.h"
+#include "vrl_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_error[512];
+
+vrl_status fail(vrl_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 52;
+
+// Dimensions and window.
+vrl_status check_dims(const vrl_dims *d)
+{
+    if (!d)
+        return fail(VRL_E_INVALID, "dims is NULL");
+    if (d->P < 1 || d->C < 1 || d->s_local < 1 || d->H < 1 || d->D < 1)
+        return fail(VRL_E_INVALID, "P, C, s_local, H and D must be >= 1 (P=%d C=%d s_local=%lld H=%d D=%d)",
+                    d->P, d->C, (long long)d->s_local, d->H, d->D);
+    if (d->H % d->P != 0)
+        return fail(VRL_E_INVALID, "H=%d is not divisible by P=%d", d->H, d->P);
+    if (d->C > d->s_local)
+        return fail(VRL_E_INVALID, "C=%d exceeds s_local=%lld (empty chunks)", d->C,
+                    (long long)d->s_local);
+    const int64_t hd = int64_t(d->H) * d->D;
+    if (d->s_local > kMaxElems / 3 / hd / d->P)
+        return fail(VRL_E_INVALID, "problem too large");
+    return VRL_OK;
+}
+
+vrl_status check_window(const vrl_dims *d, int32_t cb, int32_t ce)
+{
+    if (cb < 0 || ce > d->C || cb >= ce)
+        return fail(VRL_E_INVALID, "bad chunk window [%d, %d) for C=%d", cb, ce, d->C);
+    return VRL_OK;
+}
+
+// Geometry of a [rows][heads][D] view: its elements are
+// ptr + 2 * (t * st + h * sh + e) bytes.  Strides of size-1 axes are
+// irrelevant and taken as 0.
+struct Geom {
+    uintptr_t ptr;
+    int64_t rows, heads, D, st, sh;
+    bool output;
+    const char *name;
+};
+
+Geom geom(const vrl_view *v, int64_t rows, int64_t heads, int64_t D, bool output, const char *name)
+{
+    Geom g{reinterpret_cast<uintptr_t>(v->ptr), rows, heads, D, v->stride_tok, v->stride_head,
+           output, name};
+    if (rows == 1)
+        g.st = 0;
+    if (heads == 1)
+        g.sh = 0;
+    return g;
+}
+
+Geom dense(const void *p, int64_t elems, bool output, const char *name)
+{
+    return Geom{reinterpret_cast<uintptr_t>(p), 1, 1, elems, 0, 0, output, name};
+}
+
+// Byte range [lo, hi) that holds every element of the view.
+void span(const Geom &g, uintptr_t &lo, uintptr_t &hi)
+{
+    lo = g.ptr;
+    hi = g.ptr + 2 * uintptr_t((g.rows - 1) * g.st + (g.heads - 1) * g.sh + g.D);
+}
+
+// True when no two elements of the view share an address: with the axes
+// sorted by stride, each stride exceeds the reach of the faster axes.
+bool self_disjoint(const Geom &g)
+{
+    struct Ax {
+        int64_t n, s;
+    } ax[3] = {{g.D, 1}, {g.heads, g.sh}, {g.rows, g.st}};
+    std::sort(ax, ax + 3, [](const Ax &x, const Ax &y) { return x.s < y.s; });
+    int64_t reach = 0;  // largest offset reachable with the faster axes
+    for (const Ax &a : ax) {
+        if (a.n == 1)
+            continue;
+        if (a.s <= reach)
+            return false;
+        reach += (a.n - 1) * a.s;
+    }
+    return true;
+}
+
+// Outer axis (larger stride) and the width of what the inner axes cover.
+void outer_inner(const Geom &g, int64_t &outer_n, int64_t &outer_s, int64_t &width)
+{
+    if (g.st >= g.sh) {
+        outer_n = g.rows, outer_s = g.st;
+        width = (g.heads - 1) * g.sh + g.D;
+    } else {
+        outer_n = g.heads, outer_s = g.sh;
+        width = (g.rows - 1) * g.st + g.D;
+    }
+}
+
+// Conservative test that two views share no element: disjoint byte ranges,
+// or the same strides with the second view's outer slices falling into the
+// gaps between the first one's (e.g. Q/K/V column views of one fused row).
+bool disjoint(const Geom &a, const Geom &b)
+{
+    uintptr_t alo, ahi, blo, bhi;
+    span(a, alo, ahi);
+    span(b, blo, bhi);
+    if (ahi <= blo || bhi <= alo)
+        return true;
+    if (a.rows != b.rows || a.heads != b.heads || a.D != b.D || a.st != b.st || a.sh != b.sh)
+        return false;
+    int64_t n, s, w;
+    outer_inner(a, n, s, w);
+    if (n < 2 || s <= 0)
+        return false;
+    const int64_t delta = (int64_t(b.ptr) - int64_t(a.ptr)) / 2;
+    if ((int64_t(b.ptr) - int64_t(a.ptr)) % 2 != 0)
+        return false;
+    const int64_t m = ((delta % s) + s) % s;
+    return m >= w && s - m >= w;
+}
+
+vrl_status check_layout(const Geom *gs, int n)
+{
+    for (int i = 0; i < n; ++i) {
+        const Geom &g = gs[i];
+        if (g.ptr == 0)
+            return fail(VRL_E_INVALID, "%s is NULL", g.name);
+        if (g.st < 0 || g.sh < 0)
+            return fail(VRL_E_LAYOUT, "%s has a negative stride", g.name);
+        if (g.ptr % 2 != 0)
+            return fail(VRL_E_LAYOUT, "%s is not 2-byte aligned", g.name);
+        if (g.output && !self_disjoint(g))
+            return fail(VRL_E_LAYOUT, "elements of output %s overlap each other", g.name);
+    }
+    // Inputs may share memory (e.g. Q/K/V views of one fused row); an output
+    // may share none with any other argument.
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if ((gs[i].output || gs[j].output) && !disjoint(gs[i], gs[j]))
+                return fail(VRL_E_LAYOUT, "%s overlaps %s", gs[i].name, gs[j].name);
+    return VRL_OK;
+}
+
+// ---- device checks -----------------------------------------------------------
+
+std::atomic<int> g_arch_ok[256];  // 0 unknown, 1 gfx950, 2 other
+
+vrl_status check_device(int &dev)
+{
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(VRL_E_DEVICE, "no current HIP device");
+    }
+    if (dev < 0 || dev >= 256)
+        return fail(VRL_E_DEVICE, "device ordinal %d out of range", dev);
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(VRL_E_DEVICE, "cannot query device %d", dev);
+        }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st != 1)
+        return fail(VRL_E_DEVICE, "device %d is not gfx950", dev);
+    return VRL_OK;
+}
+
+// Each view must be device memory of `dev` and lie inside its allocation.
+vrl_status check_memory(const Geom *gs, int n, int dev)
+{
+    for (int i = 0; i < n; ++i) {
+        const Geom &g = gs[i];
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, reinterpret_cast<void *>(g.ptr)) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(VRL_E_DEVICE, "%s is not HIP device memory", g.name);
+        }
+        if (attr.type != hipMemoryTypeDevice || attr.device != dev)
+            return fail(VRL_E_DEVICE, "%s is not device memory of device %d", g.name, dev);
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, reinterpret_cast<hipDeviceptr_t>(g.ptr)) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return fail(VRL_E_DEVICE, "cannot find the allocation of %s", g.name);
+        }
+        uintptr_t lo, hi;
+        span(g, lo, hi);
+        const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+        if (lo < b || hi > b + size)
+            return fail(VRL_E_INVALID, "%s extends past its allocation (%zu bytes)", g.name, size);
+    }
+    return VRL_OK;
+}
+
+// ---- planning ----------------------------------------------------------------
+
+void magic_for(uint32_t d, uint64_t &magic, uint32_t &shift)
+{
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d)
+        ++l;
+    shift = 31 + l;
+    magic = ((uint64_t(1) << shift) + d - 1) / d;
+}
+
+// Largest vector width (bytes) that divides every address, stride and row.
+int vector_bytes(const Geom *gs, int n, int64_t D)
+{
+    uint64_t acc = uint64_t(D) * 2;
+    for (int i = 0; i < n; ++i) {
+        acc |= gs[i].ptr;
+        acc |= uint64_t(gs[i].st) * 2;
+        acc |= uint64_t(gs[i].sh) * 2;
+    }
+    for (int vb : {16, 8, 4})
+        if (acc % uint64_t(vb) == 0)
+            return vb;
+    return 2;
+}
+
+// Chooses the vector width and the kernel arguments (no device access).
+vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nviews,
+                     const Geom &wire, int32_t cb, int32_t ce, vrl::LaunchPlan &pl)
+{
+    const int64_t G = d->H / d->P;
+    Geom all[4];
+    for (int i = 0; i < nviews; ++i)
+        all[i] = views[i];
+    all[nviews] = wire;
+    const int vb = vector_bytes(all, nviews + 1, d->D);
+    const int ve = vb / 2;
+
+    pl = vrl::LaunchPlan{};
+    pl.op = op;
+    pl.vec_bytes = vb;
+    pl.contig = true;
+    for (int i = 0; i < nviews; ++i)
+        if (G > 1 && views[i].sh != d->D)
+            pl.contig = false;
+
+    vrl::KernelArgs &a = pl.args;
+    for (int i = 0; i < 3; ++i) {
+        const Geom &g = views[i < nviews ? i : 0];
+        a.view_ptr[i] = reinterpret_cast<uint16_t *>(g.ptr);
+        a.view_st[i] = g.st;
+        a.view_sh[i] = g.sh;
+    }
+    a.wire = reinterpret_cast<uint16_t *>(wire.ptr);
+    a.s_local = d->s_local;
+    a.G = int32_t(G);
+    a.D = d->D;
+
+    const int64_t chunk_q = d->s_local / d->C, chunk_r = d->s_local % d->C;
+    const int64_t row_vecs = G * d->D / ve;
+    const int64_t t_max = chunk_q + (chunk_r ? 1 : 0);
+    if (t_max > (int64_t(1) << 31) / row_vecs ||
+        t_max * row_vecs + int64_t(vrl::kTileVecs) >= (int64_t(1) << 31))
+        return fail(VRL_E_INVALID, "a chunk of %lld tokens x %lld vectors is too large; use more chunks",
+                    (long long)t_max, (long long)row_vecs);
+    const int64_t nvec_max = t_max * row_vecs;
+    a.chunk_q = int32_t(chunk_q);
+    a.chunk_r = int32_t(chunk_r);
+    a.c_begin = cb;
+    a.n_win = ce - cb;
+    a.row_vecs = uint32_t(row_vecs);
+    a.head_vecs = uint32_t(d->D / ve);
+    magic_for(a.row_vecs, a.row_magic, a.row_shift);
+    magic_for(a.head_vecs, a.head_magic, a.head_shift);
+    a.tiles = uint32_t((nvec_max + vrl::kTileVecs - 1) / vrl::kTileVecs);
+    const int64_t planes = (op == vrl::Op::Pack || op == vrl::Op::Unpack) ? 3 : 1;
+    const int64_t grid = int64_t(d->P) * (ce - cb) * planes * a.tiles;
+    if (grid >= (int64_t(1) << 31))
+        return fail(VRL_E_INVALID, "launch of %lld workgroups is too large", (long long)grid);
+    pl.grid = uint32_t(grid);
+    return VRL_OK;
+}
+
+vrl_status run(vrl::Op op, const vrl_dims *d, const Geom *views, int nviews, const Geom &wire,
+               int32_t cb, int32_t ce, void *stream)
+{
+    Geom all[4];
+    for (int i = 0; i < nviews; ++i)
+        all[i] = views[i];
+    all[nviews] = wire;
+    vrl_status s = check_layout(all, nviews + 1);
+    if (s != VRL_OK)
+        return s;
+    vrl::LaunchPlan pl;
+    if ((s = make_plan(op, d, views, nviews, wire, cb, ce, pl)) != VRL_OK)
+        return s;
+    int dev = 0;
+    if ((s = check_device(dev)) != VRL_OK)
+        return s;
+    if ((s = check_memory(all, nviews + 1, dev)) != VRL_OK)
+        return s;
+    const hipError_t e = vrl::launch(pl, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(VRL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return VRL_OK;
+}
+
+bool null_view(const vrl_view *v)
+{
+    return v == nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t vrl_exchange_elems(int which, const vrl_dims *dims)
+{
+    if (check_dims(dims) != VRL_OK || (which != VRL_EXCHANGE_QKV && which != VRL_EXCHANGE_ATTN))
+        return -1;
+    return (which == VRL_EXCHANGE_QKV ? 3 : 1) * dims->s_local * dims->H * dims->D;
+}
+
+int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c)
+{
+    if (check_dims(dims) != VRL_OK || c < 0 || c > dims->C)
+        return -1;
+    const int64_t q = dims->s_local / dims->C, r = dims->s_local % dims->C;
+    return int64_t(c) * q + std::min<int64_t>(c, r);
+}
+
+vrl_status vrl_qkv_pack(const vrl_dims *dims, const vrl_view *q, const vrl_view *k,
+                        const vrl_view *v, void *packed, int32_t c_begin, int32_t c_end,
+                        void *hip_stream)
+{
+    g_error[0] = 0;
+    try {
+        vrl_status s = check_dims(dims);
+        if (s == VRL_OK)
+            s = check_window(dims, c_begin, c_end);
+        if (s != VRL_OK)
+            return s;
+        if (null_view(q) || null_view(k) || null_view(v))
+            return fail(VRL_E_INVALID, "a view argument is NULL");
+        const int64_t S_l = dims->s_local, H = dims->H, D = dims->D;
+        const Geom views[3] = {geom(q, S_l, H, D, false, "q"), geom(k, S_l, H, D, false, "k"),
+                               geom(v, S_l, H, D, false, "v")};
+        const Geom wire = dense(packed, vrl_exchange_elems(VRL_EXCHANGE_QKV, dims), true, "packed");
+        return run(vrl::Op::Pack, dims, views, 3, wire, c_begin, c_end, hip_stream);
+    } catch (...) {
+        return fail(VRL_E_DEVICE, "internal error");
+    }
+}
+
+vrl_status vrl_qkv_unpack(const vrl_dims *dims, const void *recv, const vrl_view *q,
+                          const vrl_view *k, const vrl_view *v, int32_t c_begin, int32_t c_end,
+                          void *hip_stream)
+{
+    g_error[0] = 0;
+    try {
+        vrl_status s = check_dims(dims);
+        if (s == VRL_OK)
+            s = check_window(dims, c_begin, c_end);
+        if (s != VRL_OK)
+            return s;
+        if (null_view(q) || null_view(k) || null_view(v))
+            return fail(VRL_E_INVALID, "a view argument is NULL");
+        const int64_t S = int64_t(dims->P) * dims->s_local, G = dims->H / dims->P, D = dims->D;
+        const Geom views[3] = {geom(q, S, G, D, true, "q"), geom(k, S, G, D, true, "k"),
+                               geom(v, S, G, D, true, "v")};
+        const Geom wire = dense(recv, vrl_exchange_elems(VRL_EXCHANGE_QKV, dims), false, "recv");
+        return run(vrl::Op::Unpack, dims, views, 3, wire, c_begin, c_end, hip_stream);
+    } catch (...) {
+        return fail(VRL_E_DEVICE, "internal error");
+    }
+}
+
+vrl_status vrl_attn_split(const vrl_dims *dims, const vrl_view *o, void *send, int32_t c_begin,
+                          int32_t c_end, void *hip_stream)
+{
+    g_error[0] = 0;
+    try {
+        vrl_status s = check_dims(dims);
+        if (s == VRL_OK)
+            s = check_window(dims, c_begin, c_end);
+        if (s != VRL_OK)
+            return s;
+        if (null_view(o))
+            return fail(VRL_E_INVALID, "view o is NULL");
+        const int64_t S = int64_t(dims->P) * dims->s_local, G = dims->H / dims->P, D = dims->D;
+        const Geom views[1] = {geom(o, S, G, D, false, "o")};
+        const Geom wire = dense(send, vrl_exchange_elems(VRL_EXCHANGE_ATTN, dims), true, "send");
+        return run(vrl::Op::Split, dims, views, 1, wire, c_begin, c_end, hip_stream);
+    } catch (...) {
+        return fail(VRL_E_DEVICE, "internal error");
+    }
+}
+
+vrl_status vrl_head_merge(const vrl_dims *dims, const void *recv, const vrl_view *out,
+                          int32_t c_begin, int32_t c_end, void *hip_stream)
+{
+    g_error[0] = 0;
+    try {
+        vrl_status s = check_dims(dims);
+        if (s == VRL_OK)
+            s = check_window(dims, c_begin, c_end);
+        if (s != VRL_OK)
+            return s;
+        if (null_view(out))
+            return fail(VRL_E_INVALID, "view out is NULL");
+        const int64_t S_l = dims->s_local, H = dims->H, D = dims->D;
+        const Geom views[1] = {geom(out, S_l, H, D, true, "out")};
+        const Geom wire = dense(recv, vrl_exchange_elems(VRL_EXCHANGE_ATTN, dims), false, "recv");
+        return run(vrl::Op::Merge, dims, views, 1, wire, c_begin, c_end, hip_stream);
+    } catch (...) {
+        return fail(VRL_E_DEVICE, "internal error");
+    }
+}
+
+const char *vrl_status_string(vrl_status status)
+{
+    switch (status) {
+    case VRL_OK: return "VRL_OK";
+    case VRL_E_INVALID: return "VRL_E_INVALID";
+    case VRL_E_LAYOUT: return "VRL_E_LAYOUT";
+    case VRL_E_DEVICE: return "VRL_E_DEVICE";
+    }
+    return "VRL_E_UNKNOWN";
+}
+
+const char *vrl_last_error(void)
+{
+    return g_error;
+}
+
+}  // extern "C"

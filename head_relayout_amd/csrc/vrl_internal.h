@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI layer (vrl_api.cpp) and the gfx950
+// kernels (vrl_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace vrl {
+
+// Workgroup shape.  A workgroup moves one tile of kThreads * kUnroll vectors
+// of one wire block; each lane issues kUnroll independent loads before its
+// stores.  Tunable at build time.
+#ifndef VRL_THREADS
+#define VRL_THREADS 256
+#endif
+#ifndef VRL_UNROLL
+#define VRL_UNROLL 8
+#endif
+constexpr int kThreads = VRL_THREADS;
+constexpr int kUnroll = VRL_UNROLL;
+constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
+
+enum class Op : int { Pack = 0, Unpack = 1, Split = 2, Merge = 3 };
+
+// Everything a kernel needs, passed by value as the kernel argument.
+// "view" is the strided side (the caller's [rows][heads][D] tensors), "wire"
+// the dense exchange buffer.  Strides are in elements.
+struct KernelArgs {
+    uint16_t *view_ptr[3];  // per plane q/k/v (one used by split and merge)
+    int64_t view_st[3];     // token-axis stride
+    int64_t view_sh[3];     // head-axis stride
+    uint16_t *wire;
+    int64_t s_local;
+    int32_t G, D;
+    int32_t chunk_q, chunk_r;  // S_l / C and S_l % C
+    int32_t c_begin, n_win;    // chunk window [c_begin, c_begin + n_win)
+    uint32_t tiles;            // workgroups per wire block
+    uint32_t row_vecs;         // vectors per wire row (one token's G heads)
+    uint32_t head_vecs;        // vectors per head row (D elements)
+    uint32_t row_shift;        // f / row_vecs == (f * row_magic) >> row_shift
+    uint64_t row_magic;
+    uint64_t head_magic;       // j / head_vecs, same scheme
+    uint32_t head_shift;
+    uint32_t pad_;
+};
+
+struct LaunchPlan {
+    Op op;
+    int vec_bytes;     // 16, 8, 4 or 2
+    bool contig;       // every view row's G heads are one contiguous run
+    uint32_t grid;     // workgroups
+    KernelArgs args;
+};
+
+// Enqueues the planned kernel on `stream`; returns the launch status.
+hipError_t launch(const LaunchPlan &plan, hipStream_t stream);
+
+}  // namespace vrl

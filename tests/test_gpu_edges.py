@@ -1,0 +1,191 @@
+"""Edge cases of the HIP path against the CPU oracle, through the C ABI.
+
+Ragged chunks, as many chunks as tokens, P = 1, 3, 4 and 8, one head per
+group, small head_dims, padded source rows whose stride forces 2-, 4- and
+8-byte vectors, a source base that is only 2-byte aligned, head-major and
+padded output views, single-chunk windows, two concurrent streams, and the
+representative P=4 attention output read head-major.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import head_relayout_amd as vrl
+import oracle
+from datagen import WORKLOADS
+from tests.gpu_harness import (SENTINEL, assert_bits_equal, assert_guard_intact, guarded,
+                               sentinel_view, to_dev)
+from tests.pipeline import dev_qkv, host_qkv, run_pipeline
+
+pytestmark = pytest.mark.gpu
+
+
+def ids_fused(P, S_l, H, D, pad=0):
+    """Per-rank fused sources holding distinct ids (never the sentinel)."""
+    hd3 = 3 * H * D
+    n = P * S_l * hd3
+    assert n < 0xFFFF
+    ids = np.arange(n, dtype=np.int64)
+    ids[ids == SENTINEL] = 0xFFFF
+    ids = ids.astype(np.uint16).reshape(P, S_l, hd3)
+    out = []
+    for r in range(P):
+        f = np.full((S_l, hd3 + pad), SENTINEL, dtype=np.uint16)
+        f[:, :hd3] = ids[r]
+        out.append(f)
+    return out
+
+
+# (P, C, S_l, H, D, source row pad)
+SHAPES = [
+    (2, 1, 64, 4, 16, 0),
+    (2, 4, 10, 4, 8, 0),
+    (3, 2, 7, 6, 8, 0),
+    (2, 5, 5, 4, 8, 0),
+    (8, 3, 9, 8, 4, 0),
+    (1, 2, 6, 3, 8, 0),
+    (4, 4, 12, 8, 2, 3),
+    (2, 3, 11, 4, 8, 1),      # odd row stride: 2-byte vectors
+    (2, 3, 11, 4, 8, 2),      # 4-byte vectors
+    (2, 3, 11, 4, 8, 4),      # 8-byte vectors
+    (2, 3, 11, 4, 128, 8),    # 16-byte vectors, padded rows
+    (2, 2, 9, 2, 200, 0),     # head_dim not a power of two, one head per group
+    (2, 7, 40, 6, 24, 0),     # 3 heads per group of 24
+]
+IDS = [f"P{s[0]}C{s[1]}S{s[2]}H{s[3]}D{s[4]}pad{s[5]}" for s in SHAPES]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=IDS)
+@pytest.mark.parametrize("layout", ["dense", "padded", "head_major"])
+def test_small_shapes(gpu, shape, layout):
+    P, C, S_l, H, D, pad = shape
+    lay = {"dense": {}, "padded": {"row_pad": 5}, "head_major": {"head_major": True}}[layout]
+    run_pipeline(gpu, P, C, S_l, H, D, ids_fused(P, S_l, H, D, pad), f"{IDS[SHAPES.index(shape)]}-{layout}",
+                 unpack_layout=lay, merge_layout=lay)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 4])
+def test_source_base_alignment(gpu, offset):
+    """A fused source starting 2, 4 or 8 bytes past a 16-byte boundary."""
+    P, C, S_l, H, D = 2, 4, 33, 4, 64
+    run_pipeline(gpu, P, C, S_l, H, D, ids_fused(P, S_l, H, D), f"offset{offset}",
+                 base_offset=offset, planes=(1,))
+
+
+def _window_case(gpu, P, C, S_l, H, D, tag):
+    G, S = H // P, P * S_l
+    od = oracle.dims(P, C, S_l, H, D)
+    rng = np.random.default_rng(7)
+    fused = rng.integers(0, 0x7F00, size=(S_l, 3 * H * D), dtype=np.uint16)
+    dq = dev_qkv(to_dev(fused, gpu), H, D)
+    n_qkv = vrl.exchange_elems(0, P, C, S_l, H, D)
+    n_att = vrl.exchange_elems(1, P, C, S_l, H, D)
+    acc, acc_whole = guarded(n_qkv, gpu)
+    for c in range(C):
+        one, _ = guarded(n_qkv, gpu)
+        vrl.qkv_pack(*dq, one, P, C, c, c + 1)
+        vrl.qkv_pack(*dq, acc, P, C, c, c + 1)
+        ref = np.full(n_qkv, SENTINEL, dtype=np.uint16)
+        oracle.qkv_pack(od, *host_qkv(fused, H, D), ref, c, c + 1)
+        torch.cuda.synchronize()
+        assert_bits_equal(one, ref, f"{tag} pack window {c}")
+    full = np.zeros(n_qkv, dtype=np.uint16)
+    oracle.qkv_pack(od, *host_qkv(fused, H, D), full)
+    assert_bits_equal(acc, full, f"{tag} pack windows composed")
+    assert_guard_intact(acc_whole, f"{tag} pack windows")
+
+    recv = acc
+    outs = [sentinel_view(S, G, D, gpu) for _ in range(3)]
+    for c in range(C):
+        vrl.qkv_unpack(recv, *[o[0] for o in outs], P, C, c, c + 1)
+        ref = [np.full((S, G, D), SENTINEL, dtype=np.uint16) for _ in range(3)]
+        for cc in range(c + 1):
+            oracle.qkv_unpack(od, full, *ref, cc, cc + 1)
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert_bits_equal(outs[i][0], ref[i], f"{tag} unpack after window {c} plane {i}")
+
+    o_ref = np.zeros((S, G, D), dtype=np.uint16)
+    oracle.qkv_unpack(od, full, o_ref, np.zeros_like(o_ref), np.zeros_like(o_ref))
+    send, _ = guarded(n_att, gpu)
+    for c in range(C):
+        vrl.attn_split(outs[0][0], send, P, C, c, c + 1)
+        ref = np.full(n_att, SENTINEL, dtype=np.uint16)
+        for cc in range(c + 1):
+            oracle.attn_split(od, o_ref, ref, cc, cc + 1)
+        torch.cuda.synchronize()
+        assert_bits_equal(send, ref, f"{tag} split after window {c}")
+
+    ref_send = np.zeros(n_att, dtype=np.uint16)
+    oracle.attn_split(od, o_ref, ref_send)
+    out, whole = sentinel_view(S_l, H, D, gpu, row_pad=3)
+    for c in range(C):
+        vrl.head_merge(send, out, P, C, c, c + 1)
+        ref = np.full((S_l, H, D), SENTINEL, dtype=np.uint16)
+        for cc in range(c + 1):
+            oracle.head_merge(od, ref_send, ref, cc, cc + 1)
+        torch.cuda.synchronize()
+        assert_bits_equal(out, ref, f"{tag} merge after window {c}")
+    assert_guard_intact(whole, f"{tag} merge windows")
+
+
+def test_windows_ragged(gpu):
+    _window_case(gpu, 3, 4, 10, 6, 8, "windows ragged")
+
+
+def test_windows_mid_size(gpu):
+    w = WORKLOADS[2]
+    _window_case(gpu, w.P, w.C, w.s_local, w.H, w.D, "windows mid-size")
+
+
+def test_two_streams(gpu):
+    """Two ranks' packs and merges enqueued concurrently on two streams."""
+    w = WORKLOADS[2]
+    P, C, S_l, H, D = w.P, w.C, w.s_local, w.H, w.D
+    od = oracle.dims(P, C, S_l, H, D)
+    fused = [datagen.fused_source(w, r) for r in range(P)]
+    dev = [to_dev(f, gpu) for f in fused]
+    n = vrl.exchange_elems(0, P, C, S_l, H, D)
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=gpu) for _ in range(P)]
+    merged = [torch.empty(S_l, H, D, dtype=torch.bfloat16, device=gpu) for _ in range(P)]
+    recv_att = [to_dev(datagen.values(S_l * H * D, seed=9, stream=r), gpu) for r in range(P)]
+    streams = [torch.cuda.Stream() for _ in range(P)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for r in range(P):
+            vrl.qkv_pack(*dev_qkv(dev[r], H, D), outs[r], P, C, stream=streams[r])
+            vrl.head_merge(recv_att[r], merged[r], P, C, stream=streams[r])
+    torch.cuda.synchronize()
+    for r in range(P):
+        ref = np.zeros(n, dtype=np.uint16)
+        oracle.qkv_pack(od, *host_qkv(fused[r], H, D), ref)
+        assert_bits_equal(outs[r], ref, f"two streams pack rank {r}")
+        m = np.zeros((S_l, H, D), dtype=np.uint16)
+        oracle.head_merge(od, recv_att[r].view(torch.int16).cpu().numpy().view(np.uint16), m)
+        assert_bits_equal(merged[r], m, f"two streams merge rank {r}")
+
+
+@pytest.mark.parametrize("head_major", [False, True])
+def test_split_config5_attention_output(gpu, head_major):
+    """The P=4 workload's per-rank [31,008][8][128] attention output, read
+    contiguous and head-major (BHTD storage)."""
+    w = WORKLOADS[5]
+    P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+    od = oracle.dims(P, C, S_l, H, D)
+    n_att = vrl.exchange_elems(1, P, C, S_l, H, D)
+    for r in range(P):
+        o = datagen.attention_output(w, r)              # [S][G][D]
+        if head_major:
+            dev_o = to_dev(np.ascontiguousarray(o.transpose(1, 0, 2)), gpu).transpose(0, 1)
+        else:
+            dev_o = to_dev(o, gpu)
+        send, whole = guarded(n_att, gpu)
+        vrl.attn_split(dev_o, send, P, C)
+        ref = np.zeros(n_att, dtype=np.uint16)
+        oracle.attn_split(od, o, ref)
+        torch.cuda.synchronize()
+        assert_bits_equal(send, ref, f"cfg5 split rank {r} head_major={head_major}")
+        assert_guard_intact(whole, "cfg5 split")
