@@ -30,9 +30,10 @@ def test_allocation_range_query(gpu):
         base, size = ctypes.c_void_p(), ctypes.c_size_t()
         assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size),
                                          t.data_ptr() + 2 * (n // 2)) == 0
+        # the range is the allocation (a caching allocator's segment may be
+        # larger than the tensor) and contains the whole tensor
         assert base.value <= t.data_ptr()
         assert base.value + size.value >= t.data_ptr() + 2 * n
-        assert size.value <= 2 * n + (64 << 20)
     say("allocation range query ok")
 
 
