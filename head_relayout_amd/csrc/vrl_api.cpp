@@ -19,6 +19,9 @@
 #include <cstdio>
 #include <cstring>
 
+// Only the C ABI is visible outside the library (built with -fvisibility=hidden).
+#define VRL_EXPORT __attribute__((visibility("default")))
+
 namespace {
 
 thread_local char g_error[512];
@@ -279,6 +282,7 @@ vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nview
     }
     a.wire = reinterpret_cast<uint16_t *>(wire.ptr);
     a.s_local = d->s_local;
+    a.P = d->P;
     a.G = int32_t(G);
     a.D = d->D;
 
@@ -342,14 +346,14 @@ bool null_view(const vrl_view *v)
 
 extern "C" {
 
-int64_t vrl_exchange_elems(int which, const vrl_dims *dims)
+VRL_EXPORT int64_t vrl_exchange_elems(int which, const vrl_dims *dims)
 {
     if (check_dims(dims) != VRL_OK || (which != VRL_EXCHANGE_QKV && which != VRL_EXCHANGE_ATTN))
         return -1;
     return (which == VRL_EXCHANGE_QKV ? 3 : 1) * dims->s_local * dims->H * dims->D;
 }
 
-int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c)
+VRL_EXPORT int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c)
 {
     if (check_dims(dims) != VRL_OK || c < 0 || c > dims->C)
         return -1;
@@ -357,7 +361,7 @@ int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c)
     return int64_t(c) * q + std::min<int64_t>(c, r);
 }
 
-vrl_status vrl_qkv_pack(const vrl_dims *dims, const vrl_view *q, const vrl_view *k,
+VRL_EXPORT vrl_status vrl_qkv_pack(const vrl_dims *dims, const vrl_view *q, const vrl_view *k,
                         const vrl_view *v, void *packed, int32_t c_begin, int32_t c_end,
                         void *hip_stream)
 {
@@ -380,7 +384,7 @@ vrl_status vrl_qkv_pack(const vrl_dims *dims, const vrl_view *q, const vrl_view 
     }
 }
 
-vrl_status vrl_qkv_unpack(const vrl_dims *dims, const void *recv, const vrl_view *q,
+VRL_EXPORT vrl_status vrl_qkv_unpack(const vrl_dims *dims, const void *recv, const vrl_view *q,
                           const vrl_view *k, const vrl_view *v, int32_t c_begin, int32_t c_end,
                           void *hip_stream)
 {
@@ -403,7 +407,7 @@ vrl_status vrl_qkv_unpack(const vrl_dims *dims, const void *recv, const vrl_view
     }
 }
 
-vrl_status vrl_attn_split(const vrl_dims *dims, const vrl_view *o, void *send, int32_t c_begin,
+VRL_EXPORT vrl_status vrl_attn_split(const vrl_dims *dims, const vrl_view *o, void *send, int32_t c_begin,
                           int32_t c_end, void *hip_stream)
 {
     g_error[0] = 0;
@@ -424,7 +428,7 @@ vrl_status vrl_attn_split(const vrl_dims *dims, const vrl_view *o, void *send, i
     }
 }
 
-vrl_status vrl_head_merge(const vrl_dims *dims, const void *recv, const vrl_view *out,
+VRL_EXPORT vrl_status vrl_head_merge(const vrl_dims *dims, const void *recv, const vrl_view *out,
                           int32_t c_begin, int32_t c_end, void *hip_stream)
 {
     g_error[0] = 0;
@@ -445,7 +449,7 @@ vrl_status vrl_head_merge(const vrl_dims *dims, const void *recv, const vrl_view
     }
 }
 
-const char *vrl_status_string(vrl_status status)
+VRL_EXPORT const char *vrl_status_string(vrl_status status)
 {
     switch (status) {
     case VRL_OK: return "VRL_OK";
@@ -456,7 +460,7 @@ const char *vrl_status_string(vrl_status status)
     return "VRL_E_UNKNOWN";
 }
 
-const char *vrl_last_error(void)
+VRL_EXPORT const char *vrl_last_error(void)
 {
     return g_error;
 }

@@ -32,7 +32,8 @@ struct KernelArgs {
     int64_t view_sh[3];     // head-axis stride
     uint16_t *wire;
     int64_t s_local;
-    int32_t G, D;
+    int32_t P, G, D;
+    int32_t pad0_;
     int32_t chunk_q, chunk_r;  // S_l / C and S_l % C
     int32_t c_begin, n_win;    // chunk window [c_begin, c_begin + n_win)
     uint32_t tiles;            // workgroups per wire block

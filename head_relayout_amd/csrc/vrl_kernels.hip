@@ -50,6 +50,13 @@ struct Vec<2> {
     typedef uint16_t type;
 };
 
+#ifndef VRL_RANK_INNER
+#define VRL_RANK_INNER 1
+#endif
+#ifndef VRL_PLANE_INNER
+#define VRL_PLANE_INNER 0
+#endif
+
 // Streaming cache policy: every byte is touched exactly once.
 #ifndef VRL_LOAD_NT
 #define VRL_LOAD_NT 1
@@ -111,18 +118,46 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
     using V = typename Vec<VB>::type;
     constexpr int VE = VB / 2;  // BF16 elements per vector
 
-    // Workgroup -> (wire block, tile).  Blocks run rank-major, then chunk,
-    // then plane: the order of the wire buffer.
+    // Workgroup -> (rank, chunk, plane, tile).
     const uint32_t wg = blockIdx.x;
-    const uint32_t blk = wg / a.tiles;
-    const uint32_t tile = wg - blk * a.tiles;
-    uint32_t plane = 0, rest = blk;
-    if (Tr::planes3) {
-        plane = rest % 3u;
-        rest /= 3u;
+    uint32_t plane = 0, tile, rest;
+    int32_t c;
+    int64_t p;
+    if (VRL_RANK_INNER && Tr::hside) {
+        // Pack and merge: the P head groups of one token row belong to
+        // different ranks, so the rank varies fastest and neighbouring
+        // workgroups cover whole rows of the [S_l][H][D] side together.
+        p = int64_t(wg % uint32_t(a.P));
+        rest = wg / uint32_t(a.P);
+        if (Tr::planes3 && VRL_PLANE_INNER) {
+            // ... and the plane next, so that the workgroups in flight read
+            // whole fused Q|K|V rows of the source.
+            plane = rest % 3u;
+            rest /= 3u;
+            tile = rest % a.tiles;
+            rest /= a.tiles;
+        } else {
+            tile = rest % a.tiles;
+            rest /= a.tiles;
+            if (Tr::planes3) {
+                plane = rest % 3u;
+                rest /= 3u;
+            }
+        }
+        c = a.c_begin + int32_t(rest);
+    } else {
+        // Unpack and split: one rank's blocks are one contiguous token range
+        // of the [S][G][D] side; blocks run in wire-buffer order.
+        const uint32_t blk = wg / a.tiles;
+        tile = wg - blk * a.tiles;
+        rest = blk;
+        if (Tr::planes3) {
+            plane = rest % 3u;
+            rest /= 3u;
+        }
+        c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+        p = int64_t(rest / uint32_t(a.n_win));
     }
-    const int32_t c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
-    const int64_t p = int64_t(rest / uint32_t(a.n_win));
     const int64_t T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
     const int64_t off = int64_t(c) * a.chunk_q + (c < a.chunk_r ? c : a.chunk_r);
     const uint32_t nvec = uint32_t(T) * a.row_vecs;
