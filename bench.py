@@ -64,6 +64,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload id (3 = the representative shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the reference materialisation arm (torch chains, A/direct/A)")
     ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
     ap.add_argument("--reps", type=int, default=10, help="launches per kernel in --mode pmc")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -244,9 +246,195 @@ def run_bench(args):
         "copy_d2d": {"bytes": 2 * src.numel() * 2, "ms": round(copy_ms, 5), "gbs": round(copy_gbs, 1)},
         "verified": "round trip bit-exact before and after timing",
     }
+    say("[bench] head-major (BHTD) attention side")
+    result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
+    if not args.no_reference:
+        say("[bench] reference materialisation arm (A/direct/A)")
+        result["reference_arm"] = reference_arm(torch, vrl, w, ranks[0])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, ranks[0].host, nbytes)
     print(json.dumps(result), flush=True)
+
+
+# ---- the reference materialisation chains on the GPU (comparison arm) ----------
+
+def ref_pack(torch, q, k, v, P, C):
+    """stack, then each (dest, chunk) block copied into its slot of a new buffer:
+    two materialisations, as in the pages' reference chain."""
+    S_l, H, D = q.shape
+    X = torch.stack([q, k, v], 0)
+    Xv = X.view(3, S_l, P, H // P, D)
+    out = torch.empty(3 * S_l * H * D, dtype=q.dtype, device=q.device)
+    at = 0
+    for d in range(P):
+        for blk in torch.tensor_split(Xv[:, :, d], C, dim=1):
+            n = blk.numel()
+            out[at:at + n].view(blk.shape).copy_(blk)
+            at += n
+    return out
+
+
+def ref_unpack(torch, recv, P, C, S_l, G, D):
+    """per plane, cat of the received blocks: one materialisation."""
+    lens = [len(x) for x in torch.tensor_split(torch.arange(S_l), C)]
+    blocks = torch.split(recv, [3 * T * G * D for _ in range(P) for T in lens])
+    shaped = [b.view(3, T, G, D) for b, T in zip(blocks, lens * P)]
+    return [torch.cat([b[q] for b in shaped], 0) for q in range(3)]
+
+
+def ref_split(torch, o, P, C, c_begin=0, c_end=None):
+    """cat of each (dest, chunk) token slice of O: one materialisation."""
+    S, G, D = o.shape
+    Ov = o.view(P, S // P, G, D)
+    parts = []
+    for d in range(P):
+        chunks = torch.tensor_split(Ov[d], C, 0)
+        parts += [x.reshape(-1) for x in chunks[c_begin:c_end]]
+    return torch.cat(parts)
+
+
+def ref_merge(torch, recv, P, S_l, G, D):
+    """stack of the per-source head groups, then permute + contiguous: two
+    materialisations."""
+    Y = torch.stack([recv.view(P, S_l, G, D)[s] for s in range(P)], 0)
+    return Y.permute(1, 0, 2, 3).contiguous().view(S_l, P * G, D)
+
+
+def reference_arm(torch, vrl, w, rk):
+    """A/direct/A medians and incremental peak allocations of the reference
+    chains against the direct relayouts, on rank 0's buffers."""
+    P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+    bf = dict(dtype=torch.bfloat16, device=rk.fused.device)
+    T0 = vrl.chunk_offset(1, P, C, S_l, H, D)
+
+    def d_pack():
+        out = torch.empty(rk.packed.numel(), **bf)
+        vrl.qkv_pack(*rk.qkv, out, P, C)
+        return out
+
+    def d_unpack():
+        outs = [torch.empty(S, G, D, **bf) for _ in range(3)]
+        vrl.qkv_unpack(rk.recv, *outs, P, C)
+        return outs
+
+    def d_split():
+        out = torch.empty(rk.send.numel(), **bf)
+        vrl.attn_split(rk.planes[0], out, P, C)
+        return out
+
+    def d_merge():
+        out = torch.empty(S_l, H, D, **bf)
+        vrl.head_merge(rk.back, out, P, C)
+        return out
+
+    arms = {
+        "qkv_pack": (lambda: ref_pack(torch, *rk.qkv, P, C), d_pack),
+        "qkv_unpack": (lambda: ref_unpack(torch, rk.recv, P, C, S_l, G, D), d_unpack),
+        "attn_split": (lambda: ref_split(torch, rk.planes[0], P, C), d_split),
+        "head_merge": (lambda: ref_merge(torch, rk.back, P, S_l, G, D), d_merge),
+    }
+    res = {}
+    for name, (ref_fn, dir_fn) in arms.items():
+        # bit-exact agreement of the two arms
+        a, b = ref_fn(), dir_fn()
+        a = a if isinstance(a, list) else [a]
+        b = b if isinstance(b, list) else [b]
+        for x, y in zip(a, b):
+            if not torch.equal(x.reshape(-1).view(torch.int16), y.reshape(-1).view(torch.int16)):
+                raise SystemExit(f"reference and direct {name} differ")
+        del a, b
+
+        def peak(fn):
+            torch.cuda.synchronize()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            out = fn()
+            torch.cuda.synchronize()
+            p = torch.cuda.max_memory_allocated() - base
+            del out
+            return p
+
+        def med(fn, reps=7):
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                out = fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+                del out
+            return sorted(ts)[reps // 2]
+
+        for _ in range(2):
+            ref_fn(), dir_fn()
+        ra = med(ref_fn)
+        dm = med(dir_fn)
+        rb = med(ref_fn)
+        res[name] = {"reference_ms": round((ra + rb) / 2, 4), "direct_ms": round(dm, 4),
+                     "speedup": round((ra + rb) / 2 / dm, 3),
+                     "reference_peak_bytes": peak(ref_fn), "direct_peak_bytes": peak(dir_fn)}
+    # one-chunk split window (the pages' split figure is per chunk)
+    ref_c = lambda: ref_split(torch, rk.planes[0], P, C, 0, 1)
+
+    def dir_c():
+        out = torch.empty(rk.send.numel(), **bf)
+        vrl.attn_split(rk.planes[0], out, P, C, 0, 1)
+        return out
+    for _ in range(2):
+        ref_c(), dir_c()
+    ts = {}
+    for arm, fn in (("a", ref_c), ("b", dir_c), ("a2", ref_c)):
+        xs = []
+        for _ in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            xs.append(e0.elapsed_time(e1))
+            del out
+        ts[arm] = sorted(xs)[3]
+    res["attn_split_one_chunk"] = {"reference_ms": round((ts["a"] + ts["a2"]) / 2, 4),
+                                   "direct_ms": round(ts["b"], 4),
+                                   "speedup": round((ts["a"] + ts["a2"]) / 2 / ts["b"], 3),
+                                   "output_bytes": P * T0 * G * D * 2}
+    return res
+
+
+def head_major_layouts(torch, vrl, w, rk):
+    """Unpack into, and split from, attention-side tensors stored head-major
+    ([G][S][D], viewed as [S][G][D]); checked against the token-major results."""
+    P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+    bf = dict(dtype=torch.bfloat16, device=rk.fused.device)
+    hm = [torch.empty(G, S, D, **bf) for _ in range(3)]
+    views = [t.transpose(0, 1) for t in hm]
+    send = torch.empty_like(rk.send)
+    nb = op_bytes(w)
+    out = {}
+    for name, fn, nbytes in (
+            ("qkv_unpack", lambda: vrl.qkv_unpack(rk.recv, *views, P, C), nb["qkv_unpack"]),
+            ("attn_split", lambda: vrl.attn_split(views[0], send, P, C), nb["attn_split"])):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ts)[5]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+    for q in range(3):
+        if not torch.equal(views[q].reshape(-1, D).view(torch.int16).contiguous(),
+                           rk.planes[q].reshape(-1, D).view(torch.int16)):
+            raise SystemExit("head-major unpack differs from token-major unpack")
+    if not torch.equal(send.view(torch.int16), rk.send.view(torch.int16)):
+        raise SystemExit("split from head-major O differs from split from token-major O")
+    return out
 
 
 def cpu_baseline(w, host, nbytes):

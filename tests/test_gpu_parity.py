@@ -32,6 +32,18 @@ def test_pipeline_parity(cid, gpu):
 
 
 @pytest.mark.gpu
+def test_representative_shape_head_major_attention_side(gpu):
+    """The representative shape with the attention side stored head-major
+    (BHTD: Q/K/V and O as [G][S][D]): unpack writes it and split reads it."""
+    w = WORKLOADS[3]
+    fused = [datagen.fused_source(w, r) for r in range(w.P)]
+    run_pipeline(gpu, w.P, w.C, w.s_local, w.H, w.D, fused, "cfg3-bhtd",
+                 unpack_layout={"head_major": True}, planes=(2,))
+    del fused
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
 def test_config4_pad_sentinel_never_copied(gpu):
     """The 64 padding columns of the fused rows hold a sentinel that must not
     reach the packed buffer."""
