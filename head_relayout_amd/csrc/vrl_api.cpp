@@ -303,6 +303,30 @@ vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nview
     magic_for(a.row_vecs, a.row_magic, a.row_shift);
     magic_for(a.head_vecs, a.head_magic, a.head_shift);
     a.tiles = uint32_t((nvec_max + vrl::kTileVecs - 1) / vrl::kTileVecs);
+
+    // A view whose heads lie further apart than its tokens (head-major
+    // storage) makes the token and head axes swap for real.  Writing such a
+    // view row by row scatters 2*D-byte pieces over G heads; those calls go
+    // through the LDS-staged kernel, whose tiles hold TT tokens of all G heads
+    // and write each head's TT tokens as one run.  (Reading such a view
+    // piecewise costs little, so gathers stay direct unless VRL_STAGE_GATHER.)
+    bool head_major = false;
+    for (int i = 0; i < nviews; ++i)
+        if (views[i].sh > views[i].st)
+            head_major = true;
+    const bool gather = op == vrl::Op::Pack || op == vrl::Op::Split;
+    const int64_t row_bytes = G * d->D * 2;
+    const bool use_lds = VRL_SCATTER_MODE == 1 && row_bytes <= int64_t(vrl::kLdsBytes);
+    if (head_major && (!gather || VRL_STAGE_GATHER) && G > 1 &&
+        (use_lds || VRL_SCATTER_MODE == 2)) {
+        const int64_t tt = std::min<int64_t>(
+            {use_lds ? int64_t(vrl::kLdsBytes) / row_bytes : int64_t(VRL_VIEW_TOKENS), t_max, 4096});
+        pl.staged = true;
+        pl.lds_bytes = use_lds ? uint32_t(tt * row_bytes) : 0;
+        a.tile_tokens = uint32_t(tt);
+        magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
+        a.tiles = uint32_t((t_max + tt - 1) / tt);
+    }
     const int64_t planes = (op == vrl::Op::Pack || op == vrl::Op::Unpack) ? 3 : 1;
     const int64_t grid = int64_t(d->P) * (ce - cb) * planes * a.tiles;
     if (grid >= (int64_t(1) << 31))

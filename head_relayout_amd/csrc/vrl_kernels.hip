@@ -111,14 +111,22 @@ struct Traits<Op::Merge> {
     static constexpr bool gather = false, hside = true, planes3 = false;
 };
 
-template <Op OP, int VB, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
+// Position of one workgroup: wire block (rank p, chunk c, plane) and the
+// tile of that block it moves; plus the block's token count and the base
+// pointers of its wire block and of its first view row.
+struct Block {
+    int64_t T;           // tokens in the chunk
+    uint32_t tile;
+    uint32_t plane;
+    int64_t st, sh;      // the view's strides for this plane
+    uint16_t *view;      // element (first token of the chunk, first head of the group)
+    uint16_t *wire;      // first element of the wire block
+};
+
+template <Op OP>
+__device__ __forceinline__ Block locate(const KernelArgs &a)
 {
     using Tr = Traits<OP>;
-    using V = typename Vec<VB>::type;
-    constexpr int VE = VB / 2;  // BF16 elements per vector
-
-    // Workgroup -> (rank, chunk, plane, tile).
     const uint32_t wg = blockIdx.x;
     uint32_t plane = 0, tile, rest;
     int32_t c;
@@ -130,8 +138,6 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
         p = int64_t(wg % uint32_t(a.P));
         rest = wg / uint32_t(a.P);
         if (Tr::planes3 && VRL_PLANE_INNER) {
-            // ... and the plane next, so that the workgroups in flight read
-            // whole fused Q|K|V rows of the source.
             plane = rest % 3u;
             rest /= 3u;
             tile = rest % a.tiles;
@@ -158,22 +164,41 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
         c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
         p = int64_t(rest / uint32_t(a.n_win));
     }
-    const int64_t T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
+    Block b;
+    b.T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
     const int64_t off = int64_t(c) * a.chunk_q + (c < a.chunk_r ? c : a.chunk_r);
-    const uint32_t nvec = uint32_t(T) * a.row_vecs;
-    const uint32_t f0 = tile * kTileVecs;
-    if (f0 >= nvec)
-        return;
-
+    b.tile = tile;
+    b.plane = plane;
     const int64_t GD = int64_t(a.G) * a.D;
     const int64_t wire_row0 =
-        Tr::planes3 ? p * 3 * a.s_local + 3 * off + int64_t(plane) * T : p * a.s_local + off;
+        Tr::planes3 ? p * 3 * a.s_local + 3 * off + int64_t(plane) * b.T : p * a.s_local + off;
     const int64_t tok0 = Tr::hside ? off : p * a.s_local + off;
     const int64_t head0 = Tr::hside ? p * a.G : 0;
-    const int64_t st = a.view_st[plane], sh = a.view_sh[plane];
+    b.st = a.view_st[plane];
+    b.sh = a.view_sh[plane];
+    b.view = a.view_ptr[plane] + tok0 * b.st + head0 * b.sh;
+    b.wire = a.wire + wire_row0 * GD;
+    return b;
+}
 
-    uint16_t *const view = a.view_ptr[plane] + tok0 * st + head0 * sh;
-    uint16_t *const wire = a.wire + wire_row0 * GD;
+// Direct kernel: each workgroup moves kTileVecs consecutive vectors of a
+// wire block; the view side follows.  Used whenever the view's heads are
+// not stored further apart than its tokens.
+template <Op OP, int VB, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
+{
+    using Tr = Traits<OP>;
+    using V = typename Vec<VB>::type;
+    constexpr int VE = VB / 2;  // BF16 elements per vector
+
+    const Block b = locate<OP>(a);
+    const uint32_t nvec = uint32_t(b.T) * a.row_vecs;
+    const uint32_t f0 = b.tile * kTileVecs;
+    if (f0 >= nvec)
+        return;
+    const int64_t st = b.st, sh = b.sh;
+    uint16_t *const view = b.view;
+    uint16_t *const wire = b.wire;
 
     // View-side element offset of vector f of the block.
     auto view_off = [&](uint32_t f) -> int64_t {
@@ -214,13 +239,126 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
     }
 }
 
+// Staged kernel, for views stored head-major (a head's tokens lie closer
+// together than a token's heads): the token and head axes truly swap between
+// the wire rows [token][head][D] and the view's [head][token][D] runs.  A
+// workgroup takes TT tokens of one wire block with all G heads, reads them in
+// the order that is contiguous on the source side into LDS (laid out in wire
+// order), and after a barrier writes them in the order that is contiguous on
+// the destination side: wire rows for a gather, runs of TT tokens per head
+// for a scatter.  Loads are clamped into the tile so that they are never
+// predicated; only LDS writes and global stores test the tile's extent.
+template <Op OP, int VB, bool USE_LDS>
+__global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
+{
+    using Tr = Traits<OP>;
+    using V = typename Vec<VB>::type;
+    constexpr int VE = VB / 2;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    V *const lds = reinterpret_cast<V *>(lds_raw);
+
+    const Block b = locate<OP>(a);
+    const uint32_t TT = a.tile_tokens;
+    const uint32_t t0 = b.tile * TT;
+    if (int64_t(t0) >= b.T)
+        return;
+    const uint32_t tte = uint32_t(min(int64_t(TT), b.T - t0));  // tokens in this tile
+    const uint32_t nv = TT * a.row_vecs;                           // vectors of a full tile
+    const int64_t st = b.st, sh = b.sh;
+    uint16_t *const view = b.view + int64_t(t0) * st;
+    uint16_t *const wire = b.wire + int64_t(t0) * a.G * a.D;
+
+    // Wire order: i -> (t, j) with j = h * head_vecs + e; LDS index = i.
+    // View order: i -> (h, t, e); LDS index = t * row_vecs + h * head_vecs + e.
+    struct Pos {
+        uint32_t t, lds;
+        int64_t view_off;
+    };
+    auto wire_order = [&](uint32_t i) -> Pos {
+        const uint32_t t = div_magic(i, a.row_magic, a.row_shift);
+        const uint32_t j = i - t * a.row_vecs;
+        const uint32_t h = div_magic(j, a.head_magic, a.head_shift);
+        const uint32_t e = j - h * a.head_vecs;
+        return Pos{t, i, int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+    };
+    auto view_order = [&](uint32_t i) -> Pos {
+        const uint32_t h = div_magic(i, a.tv_magic, a.tv_shift);
+        const uint32_t r = i - h * (TT * a.head_vecs);
+        const uint32_t t = div_magic(r, a.head_magic, a.head_shift);
+        const uint32_t e = r - t * a.head_vecs;
+        return Pos{t, t * a.row_vecs + h * a.head_vecs + e,
+                   int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+    };
+
+    // Phase 1: source -> LDS, in the source's contiguous order.
+    for (uint32_t i0 = 0; USE_LDS && i0 < nv; i0 += kTileVecs) {
+        V buf[kUnroll];
+        uint32_t slot[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
+            const uint32_t ic = i < nv ? i : nv - 1;
+            Pos q = Tr::gather ? view_order(ic) : wire_order(ic);
+            ok[u] = i < nv && q.t < tte;
+            const uint32_t tc = q.t < tte ? q.t : tte - 1;
+            // clamp the token into the tile: the load stays in bounds
+            const V *src = Tr::gather
+                ? reinterpret_cast<const V *>(view + q.view_off - int64_t(q.t - tc) * st)
+                : reinterpret_cast<const V *>(wire + (int64_t(ic) - int64_t(q.t - tc) * a.row_vecs) * VE);
+            buf[u] = load_vec(src);
+            slot[u] = q.lds;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (ok[u])
+                lds[slot[u]] = buf[u];
+    }
+    if (USE_LDS)
+        __syncthreads();
+    // Phase 2: LDS (or, without LDS, the source itself) -> destination, in the destination's contiguous order
+    // (all LDS reads of a batch first, then the stores).
+    for (uint32_t i0 = 0; i0 < nv; i0 += kTileVecs) {
+        V buf[kUnroll];
+        int64_t doff[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
+            const uint32_t ic = i < nv ? i : nv - 1;
+            Pos q = Tr::gather ? wire_order(ic) : view_order(ic);
+            ok[u] = i < nv && q.t < tte;
+            doff[u] = Tr::gather ? int64_t(ic) * VE : q.view_off;
+            if (USE_LDS) {
+                buf[u] = lds[q.lds];
+            } else {
+                // read the source directly; the token is clamped into the tile
+                const uint32_t tc = q.t < tte ? q.t : tte - 1;
+                buf[u] = Tr::gather
+                    ? load_vec(reinterpret_cast<const V *>(view + q.view_off - int64_t(q.t - tc) * st))
+                    : load_vec(reinterpret_cast<const V *>(wire + (int64_t(q.lds) - int64_t(q.t - tc) * a.row_vecs) * VE));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (ok[u])
+                store_vec(reinterpret_cast<V *>((Tr::gather ? wire : view) + doff[u]), buf[u]);
+    }
+}
+
 template <Op OP, int VB>
 hipError_t launch_vb(const LaunchPlan &pl, hipStream_t stream)
 {
-    const void *fn = pl.contig ? reinterpret_cast<const void *>(&relayout_kernel<OP, VB, true>)
-                               : reinterpret_cast<const void *>(&relayout_kernel<OP, VB, false>);
     KernelArgs args = pl.args;
     void *kargs[] = {&args};
+    if (pl.staged)
+        return pl.lds_bytes
+            ? hipLaunchKernel(reinterpret_cast<const void *>(&staged_kernel<OP, VB, true>), dim3(pl.grid),
+                              dim3(kThreads), kargs, pl.lds_bytes, stream)
+            : hipLaunchKernel(reinterpret_cast<const void *>(&staged_kernel<OP, VB, false>), dim3(pl.grid),
+                              dim3(kThreads), kargs, 0, stream);
+    const void *fn = pl.contig ? reinterpret_cast<const void *>(&relayout_kernel<OP, VB, true>)
+                               : reinterpret_cast<const void *>(&relayout_kernel<OP, VB, false>);
     return hipLaunchKernel(fn, dim3(pl.grid), dim3(kThreads), kargs, 0, stream);
 }
 
