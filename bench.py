@@ -246,6 +246,8 @@ def run_bench(args):
         "copy_d2d": {"bytes": 2 * src.numel() * 2, "ms": round(copy_ms, 5), "gbs": round(copy_gbs, 1)},
         "verified": "round trip bit-exact before and after timing",
     }
+    say("[bench] four-chunk overlap schedule")
+    result["overlap"] = overlap_schedule(torch, w, ranks)
     say("[bench] head-major (BHTD) attention side")
     result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
     if not args.no_reference:
@@ -400,6 +402,39 @@ def reference_arm(torch, vrl, w, rk):
                                    "speedup": round((ts["a"] + ts["a2"]) / 2 / ts["b"], 3),
                                    "output_bytes": P * T0 * G * D * 2}
     return res
+
+
+def overlap_schedule(torch, w, ranks, reps=10):
+    """The whole layer, exchanges included: serial (each stage over all
+    chunks, one after the other) against the four-chunk overlap schedule
+    (per-chunk stages, exchanges on a second stream, event-ordered ready
+    waits).  Exchanges are device copies in one HBM here, so they compete
+    with the kernels for bandwidth; on several GPUs they would use the
+    links instead."""
+    from harness.ulysses import Layer, run_overlapped, run_serial
+
+    layer = Layer(w.P, w.C, w.s_local, w.H, w.D)
+    comm = torch.cuda.Stream()
+    out = {}
+    for name, fn in (("serial", lambda: run_serial(layer, ranks)),
+                     ("overlapped", lambda: run_overlapped(layer, ranks, comm))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(1e3 * (time.perf_counter() - t0) / reps, 4)
+    waits = {}
+    run_overlapped(layer, ranks, comm, waits=waits)
+    torch.cuda.synchronize()
+    for kind, pairs in waits.items():
+        out[kind + "_ready_wait_ms"] = round(sum(a.elapsed_time(b) for a, b in pairs), 4)
+    if not all(torch.equal(rk.merged.view(torch.int16), rk.qkv[0].view(torch.int16)) for rk in ranks):
+        raise SystemExit("overlap schedule: round trip is not bit-exact")
+    out["chunks"] = w.C
+    return out
 
 
 def head_major_layouts(torch, vrl, w, rk):
