@@ -66,9 +66,15 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_set_threads.argtypes = [i32]
     L.oracle_set_threads.restype = None
     L.oracle_threads.argtypes = []
+    L.oracle_qkv_pack_hc.argtypes = [D, V, V, V, P, i32, i32, i64p]
+    L.oracle_qkv_unpack_hc.argtypes = [D, P, V, V, V, i32, i32, i64p]
+    L.oracle_attn_split_hc.argtypes = [D, V, P, i32, i32, i64p]
+    L.oracle_head_merge_hc.argtypes = [D, P, V, i32, i32, i64p]
+    L.oracle_exchange_hc.argtypes = [D, i32, ctypes.POINTER(P), ctypes.POINTER(P)]
     for name in ("oracle_qkv_pack", "oracle_qkv_pack_permute", "oracle_qkv_unpack",
                  "oracle_qkv_unpack_permute", "oracle_attn_split", "oracle_head_merge",
-                 "oracle_exchange", "oracle_threads"):
+                 "oracle_exchange", "oracle_threads", "oracle_qkv_pack_hc", "oracle_qkv_unpack_hc",
+                 "oracle_attn_split_hc", "oracle_head_merge_hc", "oracle_exchange_hc"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -104,11 +110,17 @@ def exchange_elems(d: Dims, which: int) -> int:
     return (3 if which == 0 else 1) * d.s_local * d.H * d.D
 
 
-def qkv_pack(d: Dims, q, k, v, packed, c_begin=None, c_end=None) -> int:
+def _fn(name: str, chunk_heads: bool):
+    """The token-chunked chain, or with chunk_heads the head-chunked one
+    (chunks split each head group instead of the tokens)."""
+    return getattr(lib(), name + ("_hc" if chunk_heads else ""))
+
+
+def qkv_pack(d: Dims, q, k, v, packed, c_begin=None, c_end=None, chunk_heads=False) -> int:
     cb, ce = _window(d, c_begin, c_end)
     peak = ctypes.c_int64(0)
-    _check(lib().oracle_qkv_pack(ctypes.byref(d), view(q), view(k), view(v), _ptr(packed),
-                                 cb, ce, ctypes.byref(peak)), "qkv_pack")
+    _check(_fn("oracle_qkv_pack", chunk_heads)(ctypes.byref(d), view(q), view(k), view(v),
+                                               _ptr(packed), cb, ce, ctypes.byref(peak)), "qkv_pack")
     return peak.value
 
 
@@ -117,11 +129,11 @@ def qkv_pack_permute(d: Dims, q, k, v, packed) -> None:
                                          _ptr(packed)), "qkv_pack_permute")
 
 
-def qkv_unpack(d: Dims, recv, q, k, v, c_begin=None, c_end=None) -> int:
+def qkv_unpack(d: Dims, recv, q, k, v, c_begin=None, c_end=None, chunk_heads=False) -> int:
     cb, ce = _window(d, c_begin, c_end)
     peak = ctypes.c_int64(0)
-    _check(lib().oracle_qkv_unpack(ctypes.byref(d), _ptr(recv), view(q), view(k), view(v),
-                                   cb, ce, ctypes.byref(peak)), "qkv_unpack")
+    _check(_fn("oracle_qkv_unpack", chunk_heads)(ctypes.byref(d), _ptr(recv), view(q), view(k),
+                                                 view(v), cb, ce, ctypes.byref(peak)), "qkv_unpack")
     return peak.value
 
 
@@ -130,27 +142,27 @@ def qkv_unpack_permute(d: Dims, recv, q, k, v) -> None:
                                            view(v)), "qkv_unpack_permute")
 
 
-def attn_split(d: Dims, o, send, c_begin=None, c_end=None) -> int:
+def attn_split(d: Dims, o, send, c_begin=None, c_end=None, chunk_heads=False) -> int:
     cb, ce = _window(d, c_begin, c_end)
     peak = ctypes.c_int64(0)
-    _check(lib().oracle_attn_split(ctypes.byref(d), view(o), _ptr(send), cb, ce,
-                                   ctypes.byref(peak)), "attn_split")
+    _check(_fn("oracle_attn_split", chunk_heads)(ctypes.byref(d), view(o), _ptr(send), cb, ce,
+                                                 ctypes.byref(peak)), "attn_split")
     return peak.value
 
 
-def head_merge(d: Dims, recv, out, c_begin=None, c_end=None) -> int:
+def head_merge(d: Dims, recv, out, c_begin=None, c_end=None, chunk_heads=False) -> int:
     cb, ce = _window(d, c_begin, c_end)
     peak = ctypes.c_int64(0)
-    _check(lib().oracle_head_merge(ctypes.byref(d), _ptr(recv), view(out), cb, ce,
-                                   ctypes.byref(peak)), "head_merge")
+    _check(_fn("oracle_head_merge", chunk_heads)(ctypes.byref(d), _ptr(recv), view(out), cb, ce,
+                                                 ctypes.byref(peak)), "head_merge")
     return peak.value
 
 
-def exchange(d: Dims, which: int, sends, recvs) -> None:
+def exchange(d: Dims, which: int, sends, recvs, chunk_heads=False) -> None:
     arr = ctypes.c_void_p * d.P
     s = arr(*[_ptr(x) for x in sends])
     r = arr(*[_ptr(x) for x in recvs])
-    _check(lib().oracle_exchange(ctypes.byref(d), which, s, r), "exchange")
+    _check(_fn("oracle_exchange", chunk_heads)(ctypes.byref(d), which, s, r), "exchange")
 
 
 def set_threads(n: int) -> None:

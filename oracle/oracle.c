@@ -260,6 +260,27 @@ static tv tv_cat0(acct *a, const tv *parts, int n)
     return out;
 }
 
+/* torch.cat(list, dim) */
+static tv tv_cat(acct *a, const tv *parts, int n, int dim)
+{
+    int64_t size[MAXD];
+    for (int k = 0; k < parts[0].ndim; ++k)
+        size[k] = parts[0].size[k];
+    size[dim] = 0;
+    for (int i = 0; i < n; ++i)
+        size[dim] += parts[i].size[dim];
+    int64_t numel = 1;
+    for (int k = 0; k < parts[0].ndim; ++k)
+        numel *= size[k];
+    tv out = tv_dense(mat_alloc(a, numel), parts[0].ndim, size);
+    int64_t at = 0;
+    for (int i = 0; i < n; ++i) {
+        tv_copy(tv_narrow(out, dim, at, parts[i].size[dim]), parts[i]);
+        at += parts[i].size[dim];
+    }
+    return out;
+}
+
 /* ---- chunking: torch.tensor_split(tokens, C) sizes ------------------------ */
 
 static int64_t chunk_len(const odims *d, int c)
@@ -529,6 +550,182 @@ int oracle_exchange(const odims *d, int which, uint16_t *const *send, uint16_t *
                 int64_t sz[1] = {n};
                 tv_copy(tv_dense(recv[r] + wire_block_start(d, s, c, per_token), 1, sz),
                         tv_dense(send[s] + wire_block_start(d, r, c, per_token), 1, sz));
+            }
+    return 0;
+}
+
+/* ---- head-chunked layout ----------------------------------------------------
+ *
+ * The other reading of the four-chunk layout: the C chunks split each
+ * destination's head group (Gc = G / C heads per chunk) instead of its
+ * tokens.  Wire blocks then hold all S_l tokens: the QKV buffer is
+ * [P][C][3][S_l][Gc][D] and the return buffer [P][C][S_l][Gc][D].  Windows
+ * select head chunks.
+ */
+
+static int hc_ok(const odims *d, int c_begin, int c_end)
+{
+    if (d->P < 1 || d->C < 1 || d->H < 1 || d->D < 1 || d->s_local < 1)
+        return 0;
+    if (d->H % d->P != 0 || (d->H / d->P) % d->C != 0)
+        return 0;
+    if (c_begin < 0 || c_end > d->C || c_begin >= c_end)
+        return 0;
+    return 1;
+}
+
+/* Element offset of block (x, c): blocks of `blk` elements, x-major. */
+static int64_t hc_block_start(const odims *d, int x, int c, int64_t blk)
+{
+    int64_t at = 0;
+    for (int xx = 0; xx < d->P; ++xx)
+        for (int cc = 0; cc < d->C; ++cc) {
+            if (xx == x && cc == c)
+                return at;
+            at += blk;
+        }
+    return at;
+}
+
+/*
+ * QKV pack, head-chunked:
+ *   X = stack([q, k, v])                     -> [3][S_l][H][D]
+ *   Xv = X.view(3, S_l, P, C, Gc, D)
+ *   packed[block(d, c)] .copy_( Xv[:, :, d, c] )   -> [3][S_l][Gc][D]
+ */
+int oracle_qkv_pack_hc(const odims *d, const oview3 *q, const oview3 *k, const oview3 *v,
+                       uint16_t *packed, int c_begin, int c_end, int64_t *peak_bytes)
+{
+    if (!hc_ok(d, c_begin, c_end) || !q->ptr || !k->ptr || !v->ptr || !packed)
+        return -1;
+    acct a = {0, 0};
+    const int64_t G = d->H / d->P, Gc = G / d->C, D = d->D, S_l = d->s_local;
+    tv src[3] = {view3(q, S_l, d->H, D), view3(k, S_l, d->H, D), view3(v, S_l, d->H, D)};
+    tv X = tv_stack(&a, src, 3);
+    tv Xv = tv_unflatten(tv_unflatten(X, 2, d->P, G), 3, d->C, Gc); /* [3][S_l][P][C][Gc][D] */
+    acct_add(&a, (int64_t)d->P * (c_end - c_begin) * 3 * S_l * Gc * D * 2);
+    for (int dd = 0; dd < d->P; ++dd)
+        for (int c = c_begin; c < c_end; ++c) {
+            tv blk = tv_select(tv_select(Xv, 2, dd), 2, c); /* [3][S_l][Gc][D] */
+            int64_t bs[4] = {3, S_l, Gc, D};
+            tv_copy(tv_dense(packed + hc_block_start(d, dd, c, 3 * S_l * Gc * D), 4, bs), blk);
+        }
+    mat_free(&a, X.data, tv_numel(&X));
+    if (peak_bytes)
+        *peak_bytes = a.peak;
+    return 0;
+}
+
+/*
+ * QKV unpack, head-chunked: per plane q,
+ *   Y_s = cat([recv[s][c][q] for c in window], dim=1)   -> [S_l][W*Gc][D]
+ *   Xq  = cat([Y_s for s], dim=0)                       -> [S][W*Gc][D]
+ *   out_q[:, window heads] .copy_( Xq )
+ */
+int oracle_qkv_unpack_hc(const odims *d, const uint16_t *recv, const oview3 *q, const oview3 *k,
+                         const oview3 *v, int c_begin, int c_end, int64_t *peak_bytes)
+{
+    if (!hc_ok(d, c_begin, c_end) || !recv || !q->ptr || !k->ptr || !v->ptr)
+        return -1;
+    acct a = {0, 0};
+    const int64_t G = d->H / d->P, Gc = G / d->C, D = d->D, S_l = d->s_local, S = d->P * S_l;
+    const int W = c_end - c_begin;
+    const oview3 *outs[3] = {q, k, v};
+    tv *chunks = (tv *)malloc(sizeof(tv) * (size_t)W);
+    tv *ranks = (tv *)malloc(sizeof(tv) * (size_t)d->P);
+    for (int qi = 0; qi < 3; ++qi) {
+        for (int s = 0; s < d->P; ++s) {
+            for (int c = c_begin; c < c_end; ++c) {
+                int64_t bs[4] = {3, S_l, Gc, D};
+                tv blk = tv_dense((uint16_t *)recv + hc_block_start(d, s, c, 3 * S_l * Gc * D), 4, bs);
+                chunks[c - c_begin] = tv_select(blk, 0, qi);
+            }
+            ranks[s] = tv_cat(&a, chunks, W, 1);
+        }
+        tv Xq = tv_cat(&a, ranks, d->P, 0);
+        for (int s = 0; s < d->P; ++s)
+            mat_free(&a, ranks[s].data, tv_numel(&ranks[s]));
+        tv_copy(tv_narrow(view3(outs[qi], S, G, D), 1, c_begin * Gc, W * Gc), Xq);
+        mat_free(&a, Xq.data, tv_numel(&Xq));
+    }
+    free(chunks);
+    free(ranks);
+    if (peak_bytes)
+        *peak_bytes = a.peak;
+    return 0;
+}
+
+/*
+ * Attention-result split, head-chunked:
+ *   Ov = O.view(P, S_l, C, Gc, D)
+ *   send[block(d, c)] .copy_( Ov[d, :, c] )          -> [S_l][Gc][D]
+ */
+int oracle_attn_split_hc(const odims *d, const oview3 *o, uint16_t *send, int c_begin, int c_end,
+                         int64_t *peak_bytes)
+{
+    if (!hc_ok(d, c_begin, c_end) || !o->ptr || !send)
+        return -1;
+    acct a = {0, 0};
+    const int64_t G = d->H / d->P, Gc = G / d->C, D = d->D, S_l = d->s_local;
+    tv Ov = tv_unflatten(tv_unflatten(view3(o, d->P * S_l, G, D), 0, d->P, S_l), 2, d->C, Gc);
+    acct_add(&a, (int64_t)d->P * (c_end - c_begin) * S_l * Gc * D * 2);
+    for (int dd = 0; dd < d->P; ++dd)
+        for (int c = c_begin; c < c_end; ++c) {
+            tv src = tv_select(tv_select(Ov, 0, dd), 1, c); /* [S_l][Gc][D] */
+            int64_t bs[3] = {S_l, Gc, D};
+            tv_copy(tv_dense(send + hc_block_start(d, dd, c, S_l * Gc * D), 3, bs), src);
+        }
+    if (peak_bytes)
+        *peak_bytes = a.peak;
+    return 0;
+}
+
+/*
+ * Returned-head merge, head-chunked:
+ *   Y = stack([recv[s][window chunks] ([W][S_l][Gc][D]) for s])  -> [P][W][S_l][Gc][D]
+ *   Z = Y.permute(2, 0, 1, 3, 4).contiguous()                    -> [S_l][P][W][Gc][D]
+ *   out.view(S_l, P, C, Gc, D)[:, :, window] .copy_( Z )
+ */
+int oracle_head_merge_hc(const odims *d, const uint16_t *recv, const oview3 *out, int c_begin,
+                         int c_end, int64_t *peak_bytes)
+{
+    if (!hc_ok(d, c_begin, c_end) || !recv || !out->ptr)
+        return -1;
+    acct a = {0, 0};
+    const int64_t G = d->H / d->P, Gc = G / d->C, D = d->D, S_l = d->s_local;
+    const int W = c_end - c_begin;
+    tv *parts = (tv *)malloc(sizeof(tv) * (size_t)d->P);
+    for (int s = 0; s < d->P; ++s) {
+        int64_t bs[4] = {W, S_l, Gc, D};
+        parts[s] = tv_dense((uint16_t *)recv + hc_block_start(d, s, c_begin, S_l * Gc * D), 4, bs);
+    }
+    tv Y = tv_stack(&a, parts, d->P);
+    static const int perm[5] = {2, 0, 1, 3, 4};
+    tv Z = tv_contiguous(&a, tv_permute(Y, perm));
+    tv O = tv_unflatten(tv_unflatten(view3(out, S_l, d->H, D), 1, d->P, G), 2, d->C, Gc);
+    tv_copy(tv_narrow(O, 2, c_begin, W), Z);
+    mat_free(&a, Z.data, tv_numel(&Z));
+    mat_free(&a, Y.data, tv_numel(&Y));
+    free(parts);
+    if (peak_bytes)
+        *peak_bytes = a.peak;
+    return 0;
+}
+
+/* Exchange of head-chunked wire buffers: block (r, c) of sender s becomes
+ * block (s, c) of receiver r. */
+int oracle_exchange_hc(const odims *d, int which, uint16_t *const *send, uint16_t *const *recv)
+{
+    if (!hc_ok(d, 0, d->C) || (which != 0 && which != 1))
+        return -1;
+    const int64_t Gc = d->H / d->P / d->C;
+    const int64_t blk = (which == 0 ? 3 : 1) * d->s_local * Gc * d->D;
+    for (int s = 0; s < d->P; ++s)
+        for (int r = 0; r < d->P; ++r)
+            for (int c = 0; c < d->C; ++c) {
+                int64_t sz[1] = {blk};
+                tv_copy(tv_dense(recv[r] + hc_block_start(d, s, c, blk), 1, sz),
+                        tv_dense(send[s] + hc_block_start(d, r, c, blk), 1, sz));
             }
     return 0;
 }

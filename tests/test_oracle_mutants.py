@@ -125,3 +125,71 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                            str(so), str(mutated)])
     with oracle.library(str(so)):
         assert not _pins_hold(), f"no pin caught the mutant: {name}"
+
+
+# ---- head-chunked chains -------------------------------------------------------
+
+MUTANTS_HC = {
+    "head-chunk pack reverses the chunks":
+        ("tv_select(tv_select(Xv, 2, dd), 2, c)", "tv_select(tv_select(Xv, 2, dd), 2, d->C - 1 - c)"),
+    "head-chunk unpack writes every window at head 0":
+        ("tv_narrow(view3(outs[qi], S, G, D), 1, c_begin * Gc, W * Gc)",
+         "tv_narrow(view3(outs[qi], S, G, D), 1, 0, W * Gc)"),
+    "head-chunk split always reads chunk 0":
+        ("tv_select(tv_select(Ov, 0, dd), 1, c)", "tv_select(tv_select(Ov, 0, dd), 1, 0)"),
+    "head-chunk merge reverses the sources":
+        ("hc_block_start(d, s, c_begin, S_l * Gc * D), 4, bs)",
+         "hc_block_start(d, d->P - 1 - s, c_begin, S_l * Gc * D), 4, bs)"),
+}
+
+HC_PIN_SHAPES = [(2, 2, 6, 8, 8, 0), (3, 2, 5, 12, 8, 1)]
+
+
+def _hc_pins_hold() -> bool:
+    HC = dict(chunk_heads=True)
+    try:
+        for P, C, S_l, H, D, pad in HC_PIN_SHAPES:
+            G, S = H // P, P * S_l
+            d = oracle.dims(P, C, S_l, H, D)
+            q, k, v = qkv_views(unique_fused(1, S_l, H, D, pad)[0], H, D)
+            packed = np.full(oracle.exchange_elems(d, 0), SENTINEL, dtype=np.uint16)
+            oracle.qkv_pack(d, q, k, v, packed, **HC)
+            np.testing.assert_array_equal(packed, im.pack_hc(P, C, S_l, H, D, (q, k, v)))
+            recv = unique_ids(3 * S_l * H * D)
+            for c in range(C):
+                got = [padded_view(S, G, D) for _ in range(3)]
+                oracle.qkv_unpack(d, recv, *[g[0] for g in got], c, c + 1, **HC)
+                want = [padded_view(S, G, D) for _ in range(3)]
+                im.unpack_hc(P, C, S_l, H, D, recv, [w[0] for w in want], (c, c + 1))
+                for a, b in zip(got, want):
+                    np.testing.assert_array_equal(a[1], b[1])
+            o = np.ascontiguousarray(unique_ids(S * G * D).reshape(S, G, D))
+            send = np.full(oracle.exchange_elems(d, 1), SENTINEL, dtype=np.uint16)
+            oracle.attn_split(d, o, send, **HC)
+            np.testing.assert_array_equal(send, im.split_hc(P, C, S_l, H, D, o))
+            m, mb = padded_view(S_l, H, D, row_pad=pad)
+            oracle.head_merge(d, send, m, **HC)
+            w, wb = padded_view(S_l, H, D, row_pad=pad)
+            im.merge_hc(P, C, S_l, H, D, send, w)
+            np.testing.assert_array_equal(mb, wb)
+    except AssertionError:
+        return False
+    return True
+
+
+def test_head_chunk_pins_hold_for_the_oracle():
+    assert _hc_pins_hold()
+
+
+@pytest.mark.parametrize("name", list(MUTANTS_HC))
+def test_head_chunk_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS_HC[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique or missing: {old!r}"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-std=c11", "-O1", "-fopenmp", "-fPIC", "-shared", "-o",
+                           str(so), str(mutated)])
+    with oracle.library(str(so)):
+        assert not _hc_pins_hold(), f"no pin caught the mutant: {name}"

@@ -43,3 +43,33 @@ def merge(P, C, S_l, H, D, recv):
     G = H // P
     Y = torch.stack([recv.view(P, S_l, G, D)[s] for s in range(P)], 0)   # [P][S_l][G][D]
     return Y.permute(1, 0, 2, 3).contiguous().view(S_l, H, D)
+
+
+# ---- head-chunk reading: chunks split each head group (torch.tensor_split on heads)
+
+def pack_hc(P, C, S_l, H, D, q, k, v):
+    G = H // P
+    Xv = torch.stack([q, k, v], 0).view(3, S_l, P, G, D)
+    blocks = [blk.contiguous().reshape(-1) for d in range(P)
+              for blk in torch.tensor_split(Xv[:, :, d], C, dim=2)]
+    return torch.cat(blocks)
+
+
+def unpack_hc(P, C, S_l, H, D, recv):
+    Gc = H // P // C
+    blocks = recv.view(P, C, 3, S_l, Gc, D)
+    return [torch.cat([torch.cat([blocks[s, c, q] for c in range(C)], 1) for s in range(P)], 0)
+            for q in range(3)]
+
+
+def split_hc(P, C, S_l, H, D, O):
+    G = H // P
+    Ov = O.reshape(P, S_l, G, D)
+    return torch.cat([blk.contiguous().reshape(-1) for d in range(P)
+                      for blk in torch.tensor_split(Ov[d], C, dim=1)])
+
+
+def merge_hc(P, C, S_l, H, D, recv):
+    Gc = H // P // C
+    Y = recv.view(P, C, S_l, Gc, D)
+    return Y.permute(2, 0, 1, 3, 4).contiguous().view(S_l, H, D)
