@@ -66,10 +66,15 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the reference materialisation arm (torch chains, A/direct/A)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed step: skip the overlap, head-chunk, head-major and "
+                         "reference sections (for profiler runs)")
     ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
     ap.add_argument("--reps", type=int, default=10, help="launches per kernel in --mode pmc")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output trees (FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats output tree")
     return ap.parse_args()
 
 
@@ -246,11 +251,14 @@ def run_bench(args):
         "copy_d2d": {"bytes": 2 * src.numel() * 2, "ms": round(copy_ms, 5), "gbs": round(copy_gbs, 1)},
         "verified": "round trip bit-exact before and after timing",
     }
-    say("[bench] four-chunk overlap schedule")
-    result["overlap"] = overlap_schedule(torch, w, ranks)
-    say("[bench] head-major (BHTD) attention side")
-    result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
-    if not args.no_reference:
+    if not args.no_extras:
+        say("[bench] four-chunk overlap schedule")
+        result["overlap"] = overlap_schedule(torch, w, ranks)
+        say("[bench] head-chunked layout")
+        result["head_chunks"] = head_chunk_layout(torch, vrl, w, ranks)
+        say("[bench] head-major (BHTD) attention side")
+        result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
+    if not args.no_reference and not args.no_extras:
         say("[bench] reference materialisation arm (A/direct/A)")
         result["reference_arm"] = reference_arm(torch, vrl, w, ranks[0])
     if not args.no_cpu_baseline:
@@ -437,6 +445,63 @@ def overlap_schedule(torch, w, ranks, reps=10):
     return out
 
 
+def _median_ms(torch, fn, reps=10):
+    for _ in range(3):
+        fn()
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in pairs)[reps // 2]
+
+
+def head_chunk_layout(torch, vrl, w, ranks):
+    """The four relayouts with the chunks splitting head groups (chunk_heads),
+    on the same tensors, with a real exchange between the ranks' wire buffers;
+    the round trip is checked bit-exact."""
+    P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+    hc = dict(chunk_heads=True)
+    bf = dict(dtype=torch.bfloat16, device=ranks[0].fused.device)
+    packed = [torch.empty_like(rk.packed) for rk in ranks]
+    recv = [torch.empty_like(rk.packed) for rk in ranks]
+    planes = [[torch.empty(S, G, D, **bf) for _ in range(3)] for _ in ranks]
+    send = [torch.empty_like(rk.send) for rk in ranks]
+    back = [torch.empty_like(rk.send) for rk in ranks]
+    merged = [torch.empty(S_l, H, D, **bf) for _ in ranks]
+    for r, rk in enumerate(ranks):
+        vrl.qkv_pack(*rk.qkv, packed[r], P, C, **hc)
+    exchange(packed, recv, P)
+    for r in range(P):
+        vrl.qkv_unpack(recv[r], *planes[r], P, C, **hc)
+        vrl.attn_split(planes[r][0], send[r], P, C, **hc)
+    exchange(send, back, P)
+    for r in range(P):
+        vrl.head_merge(back[r], merged[r], P, C, **hc)
+    torch.cuda.synchronize()
+    for r, rk in enumerate(ranks):
+        if not torch.equal(merged[r].view(torch.int16), rk.qkv[0].view(torch.int16)):
+            raise SystemExit("head-chunked round trip is not bit-exact")
+        if not all(torch.equal(planes[r][q].view(torch.int16), rk.planes[q].view(torch.int16))
+                   for q in range(3)):
+            raise SystemExit("head-chunked unpack differs from token-chunked unpack")
+    nb = op_bytes(w)
+    out = {}
+    for name, fn in (("qkv_pack", lambda: vrl.qkv_pack(*ranks[0].qkv, packed[0], P, C, **hc)),
+                     ("qkv_unpack", lambda: vrl.qkv_unpack(recv[0], *planes[0], P, C, **hc)),
+                     ("attn_split", lambda: vrl.attn_split(planes[0][0], send[0], P, C, **hc)),
+                     ("head_merge", lambda: vrl.head_merge(back[0], merged[0], P, C, **hc))):
+        ms = _median_ms(torch, fn)
+        gbs = nb[name] / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+    ms = _median_ms(torch, lambda: vrl.attn_split(planes[0][0], send[0], P, C, 0, 1, **hc))
+    out["attn_split_one_chunk"] = {"ms": round(ms, 5), "output_bytes": S * (G // C) * D * 2}
+    return out
+
+
 def head_major_layouts(torch, vrl, w, rk):
     """Unpack into, and split from, attention-side tensors stored head-major
     ([G][S][D], viewed as [S][G][D]); checked against the token-major results."""
@@ -600,10 +665,44 @@ def pmc_summary(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+def trace_summary(d):
+    """Per-kernel table of a rocprofv3 --kernel-trace run of this benchmark,
+    one row per (kernel, grid size)."""
+    import datagen
+
+    w = datagen.WORKLOADS[3]
+    nb = op_bytes(w)
+    names = {"0": "qkv_pack", "1": "qkv_unpack", "2": "attn_split", "3": "head_merge"}
+    paths = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    groups = {}
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print(f"# kernel sources: sha256 prefix {kernel_source_hash()}")
+    print(f"{'kernel':<36} {'grid':>9} {'calls':>5} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"
+          f" {'GB/s(avg)':>10} {'%8TB/s':>7}")
+    for (name, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        avg = sum(ns) / len(ns)
+        cols = f"{grid:>9} {len(ns):>5} {avg / 1e3:9.1f} {min(ns) / 1e3:9.1f} {max(ns) / 1e3:9.1f}"
+        if "(vrl::Op)" in name:
+            op = names[name.split("(vrl::Op)")[1][0]]
+            kind = "staged" if "staged_kernel" in name else "direct"
+            gbs = nb[op] / (avg * 1e-9) / 1e9
+            print(f"{kind + ' ' + op:<36} {cols} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")
+        elif "copyBuffer" in name:
+            print(f"{'__amd_rocclr_copyBuffer (exchanges)':<36} {cols}")
+
+
 def main():
     args = parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the P ranks' "

@@ -31,8 +31,8 @@ def _torch():
     return torch
 
 
-def _dims(P, C, s_local, H, D) -> _lib.Dims:
-    return _lib.Dims(int(P), int(C), int(s_local), int(H), int(D))
+def _dims(P, C, s_local, H, D, chunk_heads=False) -> _lib.Dims:
+    return _lib.Dims(int(P), int(C), int(s_local), int(H), int(D), int(bool(chunk_heads)))
 
 
 def _view(t, name: str) -> _lib.View:
@@ -69,77 +69,81 @@ def _window(C, c_begin, c_end):
     return int(c_begin), int(C if c_end is None else c_end)
 
 
-def exchange_elems(which: int, P: int, C: int, s_local: int, H: int, D: int) -> int:
+def exchange_elems(which: int, P: int, C: int, s_local: int, H: int, D: int,
+                   chunk_heads: bool = False) -> int:
     """Elements of one rank's wire buffer (which: VRL_EXCHANGE_QKV or _ATTN)."""
-    n = _lib.lib().vrl_exchange_elems(which, ctypes.byref(_dims(P, C, s_local, H, D)))
+    n = _lib.lib().vrl_exchange_elems(which, ctypes.byref(_dims(P, C, s_local, H, D, chunk_heads)))
     if n < 0:
         raise ValueError("invalid dimensions")
     return n
 
 
-def chunk_offset(c: int, P: int, C: int, s_local: int, H: int, D: int) -> int:
-    """First local token of chunk c (c = C gives s_local)."""
-    n = _lib.lib().vrl_chunk_offset(ctypes.byref(_dims(P, C, s_local, H, D)), int(c))
+def chunk_offset(c: int, P: int, C: int, s_local: int, H: int, D: int,
+                 chunk_heads: bool = False) -> int:
+    """Start of chunk c along the chunked axis: its first local token (c = C
+    gives s_local), or with chunk_heads its first head within a head group."""
+    n = _lib.lib().vrl_chunk_offset(ctypes.byref(_dims(P, C, s_local, H, D, chunk_heads)), int(c))
     if n < 0:
         raise ValueError("invalid arguments")
     return n
 
 
 def qkv_pack(q, k, v, packed, P: int, C: int, c_begin: int = 0, c_end: int | None = None,
-             stream=None) -> None:
-    """packed[d][c][q][t][g][:] = src_q[off(c)+t][d*G+g][:]; q, k, v are [S_l][H][D]."""
+             stream=None, chunk_heads: bool = False) -> None:
+    """packed[d][c][q][t][g][:] = src_q[off(c)+t][d*G+g][:]; q, k, v are [S_l][H][D].
+    With chunk_heads the chunks split head groups (see include/vrl.h)."""
     S_l, H, D = q.shape[-3], q.shape[-2], q.shape[-1]
-    d = _dims(P, C, S_l, H, D)
+    d = _dims(P, C, S_l, H, D, chunk_heads)
     vq, vk, vv = _view(q, "q"), _view(k, "k"), _view(v, "v")
     for t, n in ((k, "k"), (v, "v")):
         if tuple(t.shape[-3:]) != (S_l, H, D):
             raise ValueError(f"{n} must have the shape of q")
     cb, ce = _window(C, c_begin, c_end)
-    ptr = _wire(packed, exchange_elems(VRL_EXCHANGE_QKV, P, C, S_l, H, D), "packed")
+    ptr = _wire(packed, exchange_elems(VRL_EXCHANGE_QKV, P, C, S_l, H, D, chunk_heads), "packed")
     _lib.check(_lib.lib().vrl_qkv_pack(ctypes.byref(d), ctypes.byref(vq), ctypes.byref(vk),
                                        ctypes.byref(vv), ptr, cb, ce, _stream(stream, q.device)),
                "vrl_qkv_pack")
 
 
 def qkv_unpack(recv, q, k, v, P: int, C: int, c_begin: int = 0, c_end: int | None = None,
-               stream=None) -> None:
+               stream=None, chunk_heads: bool = False) -> None:
     """X_q[s*S_l+off(c)+t][g][:] = recv[s][c][q][t][g][:]; q, k, v are [S][G][D] (or [1][S][G][D])."""
     S, G, D = q.shape[-3], q.shape[-2], q.shape[-1]
     if S % P:
         raise ValueError("the token count of q must be a multiple of P")
-    d = _dims(P, C, S // P, G * P, D)
+    d = _dims(P, C, S // P, G * P, D, chunk_heads)
     vq, vk, vv = _view(q, "q"), _view(k, "k"), _view(v, "v")
     for t, n in ((k, "k"), (v, "v")):
         if tuple(t.shape[-3:]) != (S, G, D):
             raise ValueError(f"{n} must have the shape of q")
     cb, ce = _window(C, c_begin, c_end)
-    ptr = _wire(recv, exchange_elems(VRL_EXCHANGE_QKV, P, C, S // P, G * P, D), "recv")
+    ptr = _wire(recv, exchange_elems(VRL_EXCHANGE_QKV, P, C, S // P, G * P, D, chunk_heads), "recv")
     _lib.check(_lib.lib().vrl_qkv_unpack(ctypes.byref(d), ptr, ctypes.byref(vq), ctypes.byref(vk),
                                          ctypes.byref(vv), cb, ce, _stream(stream, q.device)),
                "vrl_qkv_unpack")
 
 
 def attn_split(o, send, P: int, C: int, c_begin: int = 0, c_end: int | None = None,
-               stream=None) -> None:
+               stream=None, chunk_heads: bool = False) -> None:
     """send[d][c][t][g][:] = O[d*S_l+off(c)+t][g][:]; o is [S][G][D] (or [1][S][G][D])."""
     S, G, D = o.shape[-3], o.shape[-2], o.shape[-1]
     if S % P:
         raise ValueError("the token count of o must be a multiple of P")
-    d = _dims(P, C, S // P, G * P, D)
+    d = _dims(P, C, S // P, G * P, D, chunk_heads)
     vo = _view(o, "o")
     cb, ce = _window(C, c_begin, c_end)
-    ptr = _wire(send, exchange_elems(VRL_EXCHANGE_ATTN, P, C, S // P, G * P, D), "send")
+    ptr = _wire(send, exchange_elems(VRL_EXCHANGE_ATTN, P, C, S // P, G * P, D, chunk_heads), "send")
     _lib.check(_lib.lib().vrl_attn_split(ctypes.byref(d), ctypes.byref(vo), ptr, cb, ce,
                                          _stream(stream, o.device)), "vrl_attn_split")
 
 
 def head_merge(recv, out, P: int, C: int, c_begin: int = 0, c_end: int | None = None,
-               stream=None) -> None:
+               stream=None, chunk_heads: bool = False) -> None:
     """out[off(c)+t][s*G+g][:] = recv[s][c][t][g][:]; out is [S_l][H][D]."""
     S_l, H, D = out.shape[-3], out.shape[-2], out.shape[-1]
-    d = _dims(P, C, S_l, H, D)
+    d = _dims(P, C, S_l, H, D, chunk_heads)
     vo = _view(out, "out")
     cb, ce = _window(C, c_begin, c_end)
-    ptr = _wire(recv, exchange_elems(VRL_EXCHANGE_ATTN, P, C, S_l, H, D), "recv")
+    ptr = _wire(recv, exchange_elems(VRL_EXCHANGE_ATTN, P, C, S_l, H, D, chunk_heads), "recv")
     _lib.check(_lib.lib().vrl_head_merge(ctypes.byref(d), ptr, ctypes.byref(vo), cb, ce,
                                          _stream(stream, out.device)), "vrl_head_merge")

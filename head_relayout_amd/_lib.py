@@ -17,7 +17,7 @@ EXPORTS = ("vrl_exchange_elems", "vrl_chunk_offset", "vrl_qkv_pack", "vrl_qkv_un
 
 class Dims(ctypes.Structure):
     _fields_ = [("P", ctypes.c_int32), ("C", ctypes.c_int32), ("s_local", ctypes.c_int64),
-                ("H", ctypes.c_int32), ("D", ctypes.c_int32)]
+                ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("chunk_heads", ctypes.c_int32)]
 
 
 class View(ctypes.Structure):

@@ -47,9 +47,13 @@ vrl_status check_dims(const vrl_dims *d)
                     d->P, d->C, (long long)d->s_local, d->H, d->D);
     if (d->H % d->P != 0)
         return fail(VRL_E_INVALID, "H=%d is not divisible by P=%d", d->H, d->P);
-    if (d->C > d->s_local)
+    if (d->chunk_heads != 0 && d->chunk_heads != 1)
+        return fail(VRL_E_INVALID, "chunk_heads must be 0 or 1, got %d", d->chunk_heads);
+    if (!d->chunk_heads && d->C > d->s_local)
         return fail(VRL_E_INVALID, "C=%d exceeds s_local=%lld (empty chunks)", d->C,
                     (long long)d->s_local);
+    if (d->chunk_heads && (d->H / d->P) % d->C != 0)
+        return fail(VRL_E_INVALID, "head group G=%d is not divisible by C=%d", d->H / d->P, d->C);
     const int64_t hd = int64_t(d->H) * d->D;
     if (d->s_local > kMaxElems / 3 / hd / d->P)
         return fail(VRL_E_INVALID, "problem too large");
@@ -268,9 +272,11 @@ vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nview
     pl = vrl::LaunchPlan{};
     pl.op = op;
     pl.vec_bytes = vb;
+    // heads per wire row: the whole group, or one head chunk of it
+    const int64_t Gb = d->chunk_heads ? G / d->C : G;
     pl.contig = true;
     for (int i = 0; i < nviews; ++i)
-        if (G > 1 && views[i].sh != d->D)
+        if (Gb > 1 && views[i].sh != d->D)
             pl.contig = false;
 
     vrl::KernelArgs &a = pl.args;
@@ -285,10 +291,13 @@ vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nview
     a.P = d->P;
     a.G = int32_t(G);
     a.D = d->D;
+    a.C = d->C;
+    a.chunk_heads = d->chunk_heads;
+    a.row_heads = int32_t(Gb);
 
     const int64_t chunk_q = d->s_local / d->C, chunk_r = d->s_local % d->C;
-    const int64_t row_vecs = G * d->D / ve;
-    const int64_t t_max = chunk_q + (chunk_r ? 1 : 0);
+    const int64_t row_vecs = Gb * d->D / ve;
+    const int64_t t_max = d->chunk_heads ? d->s_local : chunk_q + (chunk_r ? 1 : 0);
     if (t_max > (int64_t(1) << 31) / row_vecs ||
         t_max * row_vecs + int64_t(vrl::kTileVecs) >= (int64_t(1) << 31))
         return fail(VRL_E_INVALID, "a chunk of %lld tokens x %lld vectors is too large; use more chunks",
@@ -315,9 +324,9 @@ vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nview
         if (views[i].sh > views[i].st)
             head_major = true;
     const bool gather = op == vrl::Op::Pack || op == vrl::Op::Split;
-    const int64_t row_bytes = G * d->D * 2;
+    const int64_t row_bytes = Gb * d->D * 2;
     const bool use_lds = VRL_SCATTER_MODE == 1 && row_bytes <= int64_t(vrl::kLdsBytes);
-    if (head_major && (!gather || VRL_STAGE_GATHER) && G > 1 &&
+    if (head_major && (!gather || VRL_STAGE_GATHER) && Gb > 1 &&
         (use_lds || VRL_SCATTER_MODE == 2)) {
         const int64_t tt = std::min<int64_t>(
             {use_lds ? int64_t(vrl::kLdsBytes) / row_bytes : int64_t(VRL_VIEW_TOKENS), t_max, 4096});
@@ -381,6 +390,8 @@ VRL_EXPORT int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c)
 {
     if (check_dims(dims) != VRL_OK || c < 0 || c > dims->C)
         return -1;
+    if (dims->chunk_heads)
+        return int64_t(c) * (dims->H / dims->P / dims->C);
     const int64_t q = dims->s_local / dims->C, r = dims->s_local % dims->C;
     return int64_t(c) * q + std::min<int64_t>(c, r);
 }

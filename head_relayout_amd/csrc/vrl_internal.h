@@ -54,7 +54,9 @@ struct KernelArgs {
     uint16_t *wire;
     int64_t s_local;
     int32_t P, G, D;
-    int32_t pad0_;
+    int32_t C;
+    int32_t chunk_heads;       // chunks split head groups instead of tokens
+    int32_t row_heads;         // heads per wire row: G, or G / C with chunk_heads
     int32_t chunk_q, chunk_r;  // S_l / C and S_l % C
     int32_t c_begin, n_win;    // chunk window [c_begin, c_begin + n_win)
     uint32_t tiles;            // workgroups per wire block

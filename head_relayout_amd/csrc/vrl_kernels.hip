@@ -56,6 +56,9 @@ struct Vec<2> {
 #ifndef VRL_PLANE_INNER
 #define VRL_PLANE_INNER 0
 #endif
+#ifndef VRL_CHUNK_INNER
+#define VRL_CHUNK_INNER 1
+#endif
 
 // Streaming cache policy: every byte is touched exactly once.
 #ifndef VRL_LOAD_NT
@@ -131,7 +134,30 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
     uint32_t plane = 0, tile, rest;
     int32_t c;
     int64_t p;
-    if (VRL_RANK_INNER && Tr::hside) {
+    if (VRL_CHUNK_INNER && a.chunk_heads && !Tr::gather) {
+        // Scatters with head chunks: a view row is cut into C pieces (and P
+        // pieces on the [S_l][H][D] side), so the chunk varies fastest, then
+        // the rank, and the pieces of a row are written together.  (Gathers
+        // keep the order below: for them this order multiplies the wire
+        // streams written at once, and measured slower.)
+        c = a.c_begin + int32_t(wg % uint32_t(a.n_win));
+        rest = wg / uint32_t(a.n_win);
+        if (Tr::hside) {
+            p = int64_t(rest % uint32_t(a.P));
+            rest /= uint32_t(a.P);
+            tile = rest % a.tiles;
+            rest /= a.tiles;
+            plane = Tr::planes3 ? rest : 0;
+        } else {
+            tile = rest % a.tiles;
+            rest /= a.tiles;
+            if (Tr::planes3) {
+                plane = rest % 3u;
+                rest /= 3u;
+            }
+            p = int64_t(rest);
+        }
+    } else if (VRL_RANK_INNER && Tr::hside) {
         // Pack and merge: the P head groups of one token row belong to
         // different ranks, so the rank varies fastest and neighbouring
         // workgroups cover whole rows of the [S_l][H][D] side together.
@@ -165,19 +191,30 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
         p = int64_t(rest / uint32_t(a.n_win));
     }
     Block b;
-    b.T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
-    const int64_t off = int64_t(c) * a.chunk_q + (c < a.chunk_r ? c : a.chunk_r);
     b.tile = tile;
     b.plane = plane;
-    const int64_t GD = int64_t(a.G) * a.D;
-    const int64_t wire_row0 =
-        Tr::planes3 ? p * 3 * a.s_local + 3 * off + int64_t(plane) * b.T : p * a.s_local + off;
-    const int64_t tok0 = Tr::hside ? off : p * a.s_local + off;
-    const int64_t head0 = Tr::hside ? p * a.G : 0;
+    const int64_t nq = Tr::planes3 ? 3 : 1;
+    const int64_t row = int64_t(a.row_heads) * a.D;  // elements per wire row
+    int64_t tok_off, head_off, wire_row0;
+    if (a.chunk_heads) {
+        // chunk c = heads [c*Gc, (c+1)*Gc) of the group, all S_l tokens
+        b.T = a.s_local;
+        tok_off = 0;
+        head_off = int64_t(c) * a.row_heads;
+        wire_row0 = ((p * a.C + c) * nq + plane) * a.s_local;
+    } else {
+        // chunk c = tokens [off(c), off(c) + T(c)), all G heads
+        b.T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
+        tok_off = int64_t(c) * a.chunk_q + (c < a.chunk_r ? c : a.chunk_r);
+        head_off = 0;
+        wire_row0 = p * nq * a.s_local + nq * tok_off + int64_t(plane) * b.T;
+    }
+    const int64_t tok0 = (Tr::hside ? 0 : p * a.s_local) + tok_off;
+    const int64_t head0 = (Tr::hside ? p * a.G : 0) + head_off;
     b.st = a.view_st[plane];
     b.sh = a.view_sh[plane];
     b.view = a.view_ptr[plane] + tok0 * b.st + head0 * b.sh;
-    b.wire = a.wire + wire_row0 * GD;
+    b.wire = a.wire + wire_row0 * row;
     return b;
 }
 
@@ -266,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
     const uint32_t nv = TT * a.row_vecs;                           // vectors of a full tile
     const int64_t st = b.st, sh = b.sh;
     uint16_t *const view = b.view + int64_t(t0) * st;
-    uint16_t *const wire = b.wire + int64_t(t0) * a.G * a.D;
+    uint16_t *const wire = b.wire + int64_t(t0) * a.row_heads * a.D;
 
     // Wire order: i -> (t, j) with j = h * head_vecs + e; LDS index = i.
     // View order: i -> (h, t, e); LDS index = t * row_vecs + h * head_vecs + e.

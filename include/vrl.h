@@ -42,13 +42,14 @@
  *
  * Windows.  Every relayout takes a chunk window [c_begin, c_end) with
  * 0 <= c_begin < c_end <= C; (0, C) is the whole tensor.  Only the window's
- * wire blocks, or the window's token rows of a view, are read and written;
- * everything else, including padding between a view's rows or heads, is
- * left untouched.
+ * wire blocks, and the window's token rows (with chunk_heads, head columns)
+ * of a view, are read and written; everything else, including padding
+ * between a view's rows or heads, is left untouched.
  *
  * Errors.  All validation happens before anything is enqueued; on any error
  * nothing is launched and every output is unchanged.
- *   VRL_E_INVALID  bad dimensions (P, C, S_l, H, D < 1; H % P != 0; C > S_l),
+ *   VRL_E_INVALID  bad dimensions (P, C, S_l, H, D < 1; H % P != 0; C > S_l
+ *                  for token chunks; G % C != 0 for head chunks),
  *                  a bad window, a null pointer, a size beyond the supported
  *                  range, or a view that extends past the end of its device
  *                  allocation.
@@ -78,13 +79,28 @@ typedef enum {
     VRL_E_DEVICE = 3
 } vrl_status;
 
-/* Problem size.  G = H / P must be a whole number. */
+/* Problem size.  G = H / P must be a whole number.
+ *
+ * chunk_heads selects what the C chunks of the four-chunk overlap layout
+ * split ("What is enabled" names the layout but not its axis):
+ *   0  each rank's tokens (the layout above; C <= s_local);
+ *   1  each destination's head group: chunk c holds heads [c*Gc, (c+1)*Gc)
+ *      of the group, Gc = G / C (G % C == 0), for all S_l tokens.  The wire
+ *      buffers are then [P][C][3][S_l][Gc][D] (QKV) and [P][C][S_l][Gc][D]
+ *      (return): block (d, c) starts at (d*C + c) * 3*S_l*Gc*D, resp.
+ *      (d*C + c) * S_l*Gc*D, and the four relayouts become
+ *        packed[d][c][q][t][g][e]   = src_q[t][d*G + c*Gc + g][e]
+ *        X_q[s*S_l + t][c*Gc + g][e] = recv[s][c][q][t][g][e]
+ *        send[d][c][t][g][e]        = O[d*S_l + t][c*Gc + g][e]
+ *        out[t][s*G + c*Gc + g][e]  = recv[s][c][t][g][e]
+ * Buffer sizes (vrl_exchange_elems) are the same for both. */
 typedef struct {
-    int32_t P;        /* ranks (virtual ranks on one GPU)                  */
-    int32_t C;        /* chunks of each rank's tokens                      */
-    int64_t s_local;  /* tokens per rank, after padding                    */
-    int32_t H;        /* attention heads                                   */
-    int32_t D;        /* head_dim                                          */
+    int32_t P;           /* ranks (virtual ranks on one GPU)               */
+    int32_t C;           /* chunks                                         */
+    int64_t s_local;     /* tokens per rank, after padding                 */
+    int32_t H;           /* attention heads                                */
+    int32_t D;           /* head_dim                                       */
+    int32_t chunk_heads; /* 0: chunks split tokens; 1: they split heads   */
 } vrl_dims;
 
 /* A [rows][heads][D] BF16 view; strides in elements, D stride is 1. */
@@ -100,8 +116,9 @@ enum { VRL_EXCHANGE_QKV = 0, VRL_EXCHANGE_ATTN = 1 };
  * S_l*H*D for VRL_EXCHANGE_ATTN.  Returns -1 for invalid arguments. */
 int64_t vrl_exchange_elems(int which, const vrl_dims *dims);
 
-/* First local token of chunk c, off(c), for c in [0, C] (off(C) = S_l).
- * Returns -1 for invalid arguments. */
+/* Start of chunk c along the chunked axis, for c in [0, C]: the first local
+ * token off(c) (off(C) = S_l), or with chunk_heads the first head of the
+ * chunk within a head group, c*Gc.  Returns -1 for invalid arguments. */
 int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c);
 
 /*

@@ -31,17 +31,19 @@ def _host_like(view: torch.Tensor) -> np.ndarray:
 
 
 def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layout=None,
-                 merge_layout=None, base_offset=0):
+                 merge_layout=None, base_offset=0, chunk_heads=False):
     """fused: per-rank host uint16 [S_l][3*H*D + pad] sources.
     unpack_layout / merge_layout: dict(row_pad=.., head_major=..) of the
     device output views.  base_offset: elements by which every device source
-    is shifted inside its allocation (to exercise narrow alignments)."""
+    is shifted inside its allocation (to exercise narrow alignments).
+    chunk_heads: chunks split head groups instead of tokens."""
+    hc = dict(chunk_heads=chunk_heads)
     unpack_layout = unpack_layout or {}
     merge_layout = merge_layout or {}
     G, S = H // P, P * S_l
     od = oracle.dims(P, C, S_l, H, D)
-    n_qkv = vrl.exchange_elems(vrl.VRL_EXCHANGE_QKV, P, C, S_l, H, D)
-    n_att = vrl.exchange_elems(vrl.VRL_EXCHANGE_ATTN, P, C, S_l, H, D)
+    n_qkv = vrl.exchange_elems(vrl.VRL_EXCHANGE_QKV, P, C, S_l, H, D, **hc)
+    n_att = vrl.exchange_elems(vrl.VRL_EXCHANGE_ATTN, P, C, S_l, H, D, **hc)
 
     dfused = []
     for f in fused:
@@ -52,9 +54,9 @@ def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layo
     packed, ref_packed = [], []
     for r in range(P):
         inner, whole = guarded(n_qkv, dev)
-        vrl.qkv_pack(*dev_qkv(dfused[r], H, D), inner, P, C)
+        vrl.qkv_pack(*dev_qkv(dfused[r], H, D), inner, P, C, **hc)
         ref = np.zeros(n_qkv, dtype=np.uint16)
-        oracle.qkv_pack(od, *host_qkv(fused[r], H, D), ref)
+        oracle.qkv_pack(od, *host_qkv(fused[r], H, D), ref, **hc)
         torch.cuda.synchronize()
         assert_bits_equal(inner, ref, f"{tag} pack rank {r}")
         assert_guard_intact(whole, f"{tag} pack rank {r}")
@@ -64,7 +66,7 @@ def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layo
     recv = [torch.empty_like(p) for p in packed]
     sim_exchange(packed, recv, P)
     ref_recv = [np.zeros(n_qkv, dtype=np.uint16) for _ in range(P)]
-    oracle.exchange(od, 0, ref_packed, ref_recv)
+    oracle.exchange(od, 0, ref_packed, ref_recv, **hc)
     del ref_packed, packed
     for r in range(P):
         assert_bits_equal(recv[r], ref_recv[r], f"{tag} simulated exchange rank {r}")
@@ -73,9 +75,9 @@ def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layo
     unpacked = []
     for r in range(P):
         outs = [sentinel_view(S, G, D, dev, **unpack_layout) for _ in range(3)]
-        vrl.qkv_unpack(recv[r], *[o[0] for o in outs], P, C)
+        vrl.qkv_unpack(recv[r], *[o[0] for o in outs], P, C, **hc)
         ref = [np.zeros((S, G, D), dtype=np.uint16) for _ in range(3)]
-        oracle.qkv_unpack(od, ref_recv[r], *ref)
+        oracle.qkv_unpack(od, ref_recv[r], *ref, **hc)
         torch.cuda.synchronize()
         for i in range(3):
             assert_bits_equal(outs[i][0], ref[i], f"{tag} unpack rank {r} plane {i}")
@@ -94,9 +96,9 @@ def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layo
         for r in range(P):
             o_dev, o_ref = unpacked[r][0][qi][0], unpacked[r][1][qi]
             inner, whole = guarded(n_att, dev)
-            vrl.attn_split(o_dev, inner, P, C)
+            vrl.attn_split(o_dev, inner, P, C, **hc)
             ref = np.zeros(n_att, dtype=np.uint16)
-            oracle.attn_split(od, o_ref, ref)
+            oracle.attn_split(od, o_ref, ref, **hc)
             torch.cuda.synchronize()
             assert_bits_equal(inner, ref, f"{tag} split rank {r} plane {qi}")
             assert_guard_intact(whole, f"{tag} split rank {r} plane {qi}")
@@ -105,12 +107,12 @@ def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layo
         back = [torch.empty_like(s) for s in sends]
         sim_exchange(sends, back, P)
         ref_back = [np.zeros(n_att, dtype=np.uint16) for _ in range(P)]
-        oracle.exchange(od, 1, ref_sends, ref_back)
+        oracle.exchange(od, 1, ref_sends, ref_back, **hc)
         for r in range(P):
             out, whole = sentinel_view(S_l, H, D, dev, **merge_layout)
-            vrl.head_merge(back[r], out, P, C)
+            vrl.head_merge(back[r], out, P, C, **hc)
             ref = np.zeros((S_l, H, D), dtype=np.uint16)
-            oracle.head_merge(od, ref_back[r], ref)
+            oracle.head_merge(od, ref_back[r], ref, **hc)
             torch.cuda.synchronize()
             assert_bits_equal(out, ref, f"{tag} merge rank {r} plane {qi}")
             assert_bits_equal(out, host_qkv(fused[r], H, D)[qi], f"{tag} round trip rank {r} plane {qi}")

@@ -171,3 +171,25 @@ def test_size_limits(vrl_lib):
     assert "too large" in _lib.last_error()
     # absurd totals are rejected by the dimension check
     assert pack(vrl_lib, (2, 1, 1 << 40, 56, 128), q, k, v) == INVALID
+
+
+def _dh(P, C, S, H, D):
+    return ctypes.byref(_lib.Dims(P, C, S, H, D, 1))
+
+
+def test_head_chunk_validation(vrl_lib):
+    L = vrl_lib
+    # G = 4 divisible by C = 4: fine, even with more chunks than tokens
+    dims = (2, 4, 3, 8, 8)
+    q, k, v = fused_qkv(dims)
+    assert L.vrl_qkv_pack(_dh(*dims), q, k, v, BASE + (1 << 30), 0, 4, None) == DEVICE
+    # G = 4 not divisible by C = 3
+    assert L.vrl_qkv_pack(_dh(2, 3, 9, 8, 8), q, k, v, BASE + (1 << 30), 0, 3, None) == INVALID
+    assert "not divisible" in _lib.last_error()
+    # chunk_heads other than 0 / 1
+    bad = _lib.Dims(2, 2, 8, 8, 8, 2)
+    assert L.vrl_qkv_pack(ctypes.byref(bad), q, k, v, BASE + (1 << 30), 0, 2, None) == INVALID
+    # helpers
+    assert [L.vrl_chunk_offset(_dh(2, 4, 27707, 56, 128), c) for c in range(5)] == [0, 7, 14, 21, 28]
+    assert L.vrl_exchange_elems(0, _dh(2, 4, 27707, 56, 128)) == 3 * 27707 * 56 * 128
+    assert L.vrl_exchange_elems(1, _dh(2, 3, 10, 8, 8)) == -1
