@@ -69,12 +69,14 @@ def parse_args():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed step: skip the overlap, head-chunk, head-major and "
                          "reference sections (for profiler runs)")
-    ap.add_argument("--mode", choices=["bench", "pmc"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-lds"], default="bench")
     ap.add_argument("--reps", type=int, default=10, help="launches per kernel in --mode pmc")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output trees (FETCH_SIZE, WRITE_SIZE)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats output tree")
+    ap.add_argument("--sq-summary", metavar="DIR",
+                    help="summarise a rocprofv3 --pmc output tree of SQ counters per kernel")
     return ap.parse_args()
 
 
@@ -262,7 +264,7 @@ def run_bench(args):
         say("[bench] reference materialisation arm (A/direct/A)")
         result["reference_arm"] = reference_arm(torch, vrl, w, ranks[0])
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, ranks[0].host, nbytes)
+        result["cpu_baseline"] = cpu_baseline(w, [rk.host for rk in ranks], nbytes)
     print(json.dumps(result), flush=True)
 
 
@@ -537,41 +539,54 @@ def head_major_layouts(torch, vrl, w, rk):
     return out
 
 
-def cpu_baseline(w, host, nbytes):
-    """The oracle's four chains on rank 0's inputs, once each, on the host."""
+def cpu_baseline(w, hosts, nbytes, reps=5):
+    """The oracle's four chains for every rank (one step of the workload) on
+    the host cores: one untimed pass, then `reps` timed passes; the median
+    pass gives the rate."""
     import numpy as np
 
     import oracle
 
     d = oracle.dims(w.P, w.C, w.s_local, w.H, w.D)
-    q, k, v = [host[:, i * w.H * w.D:(i + 1) * w.H * w.D].reshape(w.s_local, w.H, w.D)
+    bufs = []
+    for host in hosts:
+        qkv = [host[:, i * w.H * w.D:(i + 1) * w.H * w.D].reshape(w.s_local, w.H, w.D)
                for i in range(3)]
-    packed = np.full(oracle.exchange_elems(d, 0), 0, dtype=np.uint16)
-    planes = [np.full((w.S, w.G, w.D), 0, dtype=np.uint16) for _ in range(3)]
-    send = np.full(oracle.exchange_elems(d, 1), 0, dtype=np.uint16)
-    merged = np.full((w.s_local, w.H, w.D), 0, dtype=np.uint16)
-    say("[bench] cpu baseline: untimed warm-up pass of the pack chain")
-    oracle.qkv_pack(d, q, k, v, packed)
-    say("[bench] cpu baseline: timing the four chains")
-    times = {}
-    t = time.perf_counter()
-    oracle.qkv_pack(d, q, k, v, packed)
-    times["qkv_pack"] = time.perf_counter() - t
-    t = time.perf_counter()
-    oracle.qkv_unpack(d, packed, *planes)
-    times["qkv_unpack"] = time.perf_counter() - t
-    t = time.perf_counter()
-    oracle.attn_split(d, planes[0], send)
-    times["attn_split"] = time.perf_counter() - t
-    t = time.perf_counter()
-    oracle.head_merge(d, send, merged)
-    times["head_merge"] = time.perf_counter() - t
-    total = sum(times.values())
-    return {"value": round(sum(nbytes.values()) / total / 1e9, 3), "unit": "GB/s",
+        bufs.append((qkv, np.full(oracle.exchange_elems(d, 0), 0, dtype=np.uint16),
+                     [np.full((w.S, w.G, w.D), 0, dtype=np.uint16) for _ in range(3)],
+                     np.full(oracle.exchange_elems(d, 1), 0, dtype=np.uint16),
+                     np.full((w.s_local, w.H, w.D), 0, dtype=np.uint16)))
+
+    def one_pass():
+        t = {"qkv_pack": 0.0, "qkv_unpack": 0.0, "attn_split": 0.0, "head_merge": 0.0}
+        for qkv, packed, planes, send, merged in bufs:
+            t0 = time.perf_counter()
+            oracle.qkv_pack(d, *qkv, packed)
+            t1 = time.perf_counter()
+            oracle.qkv_unpack(d, packed, *planes)
+            t2 = time.perf_counter()
+            oracle.attn_split(d, planes[0], send)
+            t3 = time.perf_counter()
+            oracle.head_merge(d, send, merged)
+            t4 = time.perf_counter()
+            t["qkv_pack"] += t1 - t0
+            t["qkv_unpack"] += t2 - t1
+            t["attn_split"] += t3 - t2
+            t["head_merge"] += t4 - t3
+        return t
+
+    say("[bench] cpu baseline: untimed pass")
+    one_pass()
+    say(f"[bench] cpu baseline: {reps} timed passes")
+    passes = sorted((one_pass() for _ in range(reps)), key=lambda t: sum(t.values()))
+    med = passes[reps // 2]
+    total = sum(med.values())
+    return {"value": round(len(hosts) * sum(nbytes.values()) / total / 1e9, 3), "unit": "GB/s",
             "cores": oracle.threads(), "kind": "oracle",
-            "sample": "rank 0 of 2: the pack, unpack, split and merge chains once each "
-                      "(pack's receive buffer stands in for the exchanged one)",
-            "ms": {k: round(1e3 * v, 1) for k, v in times.items()}}
+            "sample": f"one step of the workload (the pack, unpack, split and merge chains for each "
+                      f"of the {len(hosts)} ranks, each rank's packed buffer standing in for its "
+                      f"exchanged one); median of {reps} timed passes after one untimed pass",
+            "ms": {k: round(1e3 * v, 1) for k, v in med.items()}}
 
 
 def read_traffic():
@@ -613,6 +628,51 @@ def run_pmc(args):
     torch.cuda.synchronize()
     print(f"pmc: {args.reps} x qkv_pack ({op_bytes(w)['qkv_pack'] // 2} B read + written), "
           f"{args.reps} x bitwise_not copy kernel ({2 * n} B read + written)", flush=True)
+
+
+def run_pmc_lds(args):
+    """The staged (LDS) unpack into head-major Q/K/V, the direct unpack into
+    token-major ones and the pack, `reps` launches each, for SQ counter runs."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import head_relayout_amd as vrl
+
+    dev = torch.device("cuda:0")
+    w = datagen.WORKLOADS[args.workload]
+    rk = Rank(w, 0, dev, torch, np, datagen, vrl)
+    rk.recv.copy_(rk.packed)
+    hm = [torch.empty(w.G, w.S, w.D, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    for _ in range(args.reps):
+        vrl.qkv_unpack(rk.recv, *[t.transpose(0, 1) for t in hm], w.P, w.C)
+    for _ in range(args.reps):
+        vrl.qkv_unpack(rk.recv, *rk.planes, w.P, w.C)
+    for _ in range(args.reps):
+        vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
+    torch.cuda.synchronize()
+    print(f"pmc-lds: {args.reps} x staged unpack (head-major), direct unpack, pack", flush=True)
+
+
+def sq_summary(d):
+    """Mean per-dispatch value of every counter in a --pmc tree, per kernel."""
+    rows = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if "(vrl::Op)" not in name:
+                    continue
+                op = {"0": "qkv_pack", "1": "qkv_unpack", "2": "attn_split",
+                      "3": "head_merge"}[name.split("(vrl::Op)")[1][0]]
+                kind = "staged" if "staged_kernel" in name else "direct"
+                rows.setdefault((kind + " " + op, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    kernels = sorted({k for k, _ in rows})
+    counters = sorted({c for _, c in rows})
+    print(f"{'kernel':<22}" + "".join(f"{c:>24}" for c in counters))
+    for k in kernels:
+        vals = [rows.get((k, c)) for c in counters]
+        print(f"{k:<22}" + "".join(f"{(sum(v) / len(v) if v else float('nan')):24.0f}" for v in vals))
 
 
 def pmc_summary(fetch_dir, write_dir):
@@ -704,6 +764,9 @@ def main():
     if args.trace_summary:
         trace_summary(args.trace_summary)
         return
+    if args.sq_summary:
+        sq_summary(args.sq_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the P ranks' "
               f"buffers and their exchange are modelled inside one GPU's HBM; a multi-GPU run "
@@ -711,6 +774,8 @@ def main():
         sys.exit(2)
     if args.mode == "pmc":
         run_pmc(args)
+    elif args.mode == "pmc-lds":
+        run_pmc_lds(args)
     else:
         run_bench(args)
 
