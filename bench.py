@@ -253,6 +253,10 @@ def run_bench(args):
         "copy_d2d": {"bytes": 2 * src.numel() * 2, "ms": round(copy_ms, 5), "gbs": round(copy_gbs, 1)},
         "verified": "round trip bit-exact before and after timing",
     }
+    say("[bench] the step captured in a HIP graph")
+    result["graph_replay"] = graph_replay(torch, ops, ranks, step_bytes, args.steps)
+    if not round_trip_ok():
+        raise SystemExit("round trip is not bit-exact after graph replays")
     if not args.no_extras:
         say("[bench] four-chunk overlap schedule")
         result["overlap"] = overlap_schedule(torch, w, ranks)
@@ -412,6 +416,37 @@ def reference_arm(torch, vrl, w, rk):
                                    "speedup": round((ts["a"] + ts["a2"]) / 2 / ts["b"], 3),
                                    "output_bytes": P * T0 * G * D * 2}
     return res
+
+
+def graph_replay(torch, ops, ranks, step_bytes, steps):
+    """The step (all four relayouts for every rank) captured once in a HIP
+    graph and replayed: the same kernels and arguments without per-launch
+    host work between them."""
+    def step():
+        for _, fn in ops:
+            for rk in ranks:
+                fn(rk)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    del g
+    return {"ms_per_step": round(ms, 4), "gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+            "steps": steps}
 
 
 def overlap_schedule(torch, w, ranks, reps=10):
