@@ -201,6 +201,8 @@ def run_bench(args):
         mean = sum(times) / len(times)
         gbs = nbytes[name] / (mean * 1e-3) / 1e9
         per_op[name] = {"ms": round(mean, 5), "ms_median": round(times[len(times) // 2], 5),
+                        "ms_p10": round(times[len(times) // 10], 5),
+                        "ms_p90": round(times[(9 * len(times)) // 10], 5),
                         "ms_min": round(times[0], 5), "bytes": nbytes[name],
                         "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
                         "launches": len(times)}
