@@ -41,8 +41,9 @@ if ROOT not in sys.path:
 METRIC = "QKV-pack / head-merge ms and effective HBM GB/s (% of peak) at 55,413 tokens"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_pack_repr55413_traffic.txt")
+# what decides the kernels' memory traffic: device code and launch planning
 KERNEL_SOURCES = ["head_relayout_amd/csrc/vrl_kernels.hip", "head_relayout_amd/csrc/vrl_internal.h",
-                  "head_relayout_amd/csrc/vrl_api.cpp"]
+                  "head_relayout_amd/csrc/vrl_plan.cpp"]
 
 
 def kernel_source_hash() -> str:

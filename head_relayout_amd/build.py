@@ -6,7 +6,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "vrl_kernels.hip"), os.path.join(CSRC, "vrl_api.cpp")]
+SOURCES = [os.path.join(CSRC, "vrl_kernels.hip"), os.path.join(CSRC, "vrl_plan.cpp"),
+           os.path.join(CSRC, "vrl_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

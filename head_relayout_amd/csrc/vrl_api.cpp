@@ -2,7 +2,7 @@
 //
 // Every check runs before anything is enqueued, in this order: dimensions and
 // window (VRL_E_INVALID), pointers and layouts (VRL_E_INVALID / VRL_E_LAYOUT),
-// the launch plan's size limits (VRL_E_INVALID), then the device and the
+// the launch plan's size limits (VRL_E_INVALID, vrl_plan.cpp), then the device and the
 // pointers' allocations (VRL_E_DEVICE / VRL_E_INVALID).  All but the last
 // group need no GPU, so they are exercised by the host-only tests.  The fail-closed behaviour (no silent fallback; layouts
 // outside the contract are reported so the caller keeps its materialising
@@ -154,6 +154,10 @@ bool disjoint(const Geom &a, const Geom &b)
     return m >= w && s - m >= w;
 }
 
+// Largest element offset any view may reach from its base; keeps every span
+// and address computation far from 64-bit overflow.
+constexpr int64_t kMaxReach = int64_t(1) << 48;
+
 vrl_status check_layout(const Geom *gs, int n)
 {
     for (int i = 0; i < n; ++i) {
@@ -162,6 +166,10 @@ vrl_status check_layout(const Geom *gs, int n)
             return fail(VRL_E_INVALID, "%s is NULL", g.name);
         if (g.st < 0 || g.sh < 0)
             return fail(VRL_E_LAYOUT, "%s has a negative stride", g.name);
+        if ((g.rows > 1 && g.st > kMaxReach / (g.rows - 1)) ||
+            (g.heads > 1 && g.sh > kMaxReach / (g.heads - 1)) ||
+            (g.rows - 1) * g.st + (g.heads - 1) * g.sh + g.D > kMaxReach)
+            return fail(VRL_E_INVALID, "%s reaches beyond 2^48 elements", g.name);
         if (g.ptr % 2 != 0)
             return fail(VRL_E_LAYOUT, "%s is not 2-byte aligned", g.name);
         if (g.output && !self_disjoint(g))
@@ -231,119 +239,6 @@ vrl_status check_memory(const Geom *gs, int n, int dev)
     return VRL_OK;
 }
 
-// ---- planning ----------------------------------------------------------------
-
-void magic_for(uint32_t d, uint64_t &magic, uint32_t &shift)
-{
-    uint32_t l = 0;
-    while ((uint64_t(1) << l) < d)
-        ++l;
-    shift = 31 + l;
-    magic = ((uint64_t(1) << shift) + d - 1) / d;
-}
-
-// Largest vector width (bytes) that divides every address, stride and row.
-int vector_bytes(const Geom *gs, int n, int64_t D)
-{
-    uint64_t acc = uint64_t(D) * 2;
-    for (int i = 0; i < n; ++i) {
-        acc |= gs[i].ptr;
-        acc |= uint64_t(gs[i].st) * 2;
-        acc |= uint64_t(gs[i].sh) * 2;
-    }
-    for (int vb : {16, 8, 4})
-        if (acc % uint64_t(vb) == 0)
-            return vb;
-    return 2;
-}
-
-// Chooses the vector width and the kernel arguments (no device access).
-vrl_status make_plan(vrl::Op op, const vrl_dims *d, const Geom *views, int nviews,
-                     const Geom &wire, int32_t cb, int32_t ce, vrl::LaunchPlan &pl)
-{
-    const int64_t G = d->H / d->P;
-    Geom all[4];
-    for (int i = 0; i < nviews; ++i)
-        all[i] = views[i];
-    all[nviews] = wire;
-    const int vb = vector_bytes(all, nviews + 1, d->D);
-    const int ve = vb / 2;
-
-    pl = vrl::LaunchPlan{};
-    pl.op = op;
-    pl.vec_bytes = vb;
-    // heads per wire row: the whole group, or one head chunk of it
-    const int64_t Gb = d->chunk_heads ? G / d->C : G;
-    pl.contig = true;
-    for (int i = 0; i < nviews; ++i)
-        if (Gb > 1 && views[i].sh != d->D)
-            pl.contig = false;
-
-    vrl::KernelArgs &a = pl.args;
-    for (int i = 0; i < 3; ++i) {
-        const Geom &g = views[i < nviews ? i : 0];
-        a.view_ptr[i] = reinterpret_cast<uint16_t *>(g.ptr);
-        a.view_st[i] = g.st;
-        a.view_sh[i] = g.sh;
-    }
-    a.wire = reinterpret_cast<uint16_t *>(wire.ptr);
-    a.s_local = d->s_local;
-    a.P = d->P;
-    a.G = int32_t(G);
-    a.D = d->D;
-    a.C = d->C;
-    a.chunk_heads = d->chunk_heads;
-    a.row_heads = int32_t(Gb);
-
-    const int64_t chunk_q = d->s_local / d->C, chunk_r = d->s_local % d->C;
-    const int64_t row_vecs = Gb * d->D / ve;
-    const int64_t t_max = d->chunk_heads ? d->s_local : chunk_q + (chunk_r ? 1 : 0);
-    if (t_max > (int64_t(1) << 31) / row_vecs ||
-        t_max * row_vecs + int64_t(vrl::kTileVecs) >= (int64_t(1) << 31))
-        return fail(VRL_E_INVALID, "a chunk of %lld tokens x %lld vectors is too large; use more chunks",
-                    (long long)t_max, (long long)row_vecs);
-    const int64_t nvec_max = t_max * row_vecs;
-    a.chunk_q = int32_t(chunk_q);
-    a.chunk_r = int32_t(chunk_r);
-    a.c_begin = cb;
-    a.n_win = ce - cb;
-    a.row_vecs = uint32_t(row_vecs);
-    a.head_vecs = uint32_t(d->D / ve);
-    magic_for(a.row_vecs, a.row_magic, a.row_shift);
-    magic_for(a.head_vecs, a.head_magic, a.head_shift);
-    a.tiles = uint32_t((nvec_max + vrl::kTileVecs - 1) / vrl::kTileVecs);
-
-    // A view whose heads lie further apart than its tokens (head-major
-    // storage) makes the token and head axes swap for real.  Writing such a
-    // view row by row scatters 2*D-byte pieces over G heads; those calls go
-    // through the LDS-staged kernel, whose tiles hold TT tokens of all G heads
-    // and write each head's TT tokens as one run.  (Reading such a view
-    // piecewise costs little, so gathers stay direct unless VRL_STAGE_GATHER.)
-    bool head_major = false;
-    for (int i = 0; i < nviews; ++i)
-        if (views[i].sh > views[i].st)
-            head_major = true;
-    const bool gather = op == vrl::Op::Pack || op == vrl::Op::Split;
-    const int64_t row_bytes = Gb * d->D * 2;
-    const bool use_lds = VRL_SCATTER_MODE == 1 && row_bytes <= int64_t(vrl::kLdsBytes);
-    if (head_major && (!gather || VRL_STAGE_GATHER) && Gb > 1 &&
-        (use_lds || VRL_SCATTER_MODE == 2)) {
-        const int64_t tt = std::min<int64_t>(
-            {use_lds ? int64_t(vrl::kLdsBytes) / row_bytes : int64_t(VRL_VIEW_TOKENS), t_max, 4096});
-        pl.staged = true;
-        pl.lds_bytes = use_lds ? uint32_t(tt * row_bytes) : 0;
-        a.tile_tokens = uint32_t(tt);
-        magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
-        a.tiles = uint32_t((t_max + tt - 1) / tt);
-    }
-    const int64_t planes = (op == vrl::Op::Pack || op == vrl::Op::Unpack) ? 3 : 1;
-    const int64_t grid = int64_t(d->P) * (ce - cb) * planes * a.tiles;
-    if (grid >= (int64_t(1) << 31))
-        return fail(VRL_E_INVALID, "launch of %lld workgroups is too large", (long long)grid);
-    pl.grid = uint32_t(grid);
-    return VRL_OK;
-}
-
 vrl_status run(vrl::Op op, const vrl_dims *d, const Geom *views, int nviews, const Geom &wire,
                int32_t cb, int32_t ce, void *stream)
 {
@@ -354,9 +249,14 @@ vrl_status run(vrl::Op op, const vrl_dims *d, const Geom *views, int nviews, con
     vrl_status s = check_layout(all, nviews + 1);
     if (s != VRL_OK)
         return s;
+    vrl::PlanView pv[3];
+    for (int i = 0; i < nviews; ++i)
+        pv[i] = vrl::PlanView{views[i].ptr, views[i].st, views[i].sh};
+    const vrl::Problem pb{d->P, d->C, d->s_local, d->H, d->D, d->chunk_heads};
     vrl::LaunchPlan pl;
-    if ((s = make_plan(op, d, views, nviews, wire, cb, ce, pl)) != VRL_OK)
-        return s;
+    const char *why = nullptr;
+    if (!vrl::plan_launch(op, pb, pv, nviews, wire.ptr, cb, ce, pl, &why))
+        return fail(VRL_E_INVALID, "%s", why);
     int dev = 0;
     if ((s = check_device(dev)) != VRL_OK)
         return s;

@@ -82,6 +82,24 @@ struct LaunchPlan {
     KernelArgs args;
 };
 
+// Problem size (the C ABI's vrl_dims) and one operand view, as the planner
+// sees them: byte address and element strides.
+struct Problem {
+    int32_t P, C;
+    int64_t s_local;
+    int32_t H, D;
+    int32_t chunk_heads;
+};
+struct PlanView {
+    uintptr_t ptr;
+    int64_t st, sh;
+};
+
+// Plans a launch (vrl_plan.cpp).  Returns false, with *why set, when the
+// problem exceeds what one launch can index.
+bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, uintptr_t wire,
+                 int32_t c_begin, int32_t c_end, LaunchPlan &pl, const char **why);
+
 // Enqueues the planned kernel on `stream`; returns the launch status.
 hipError_t launch(const LaunchPlan &plan, hipStream_t stream);
 

@@ -1,0 +1,126 @@
+// Launch planning of the relayout kernels: vector width, kernel selection,
+// tile geometry and the kernel arguments, from the problem and the operands'
+// addresses and strides.  Pure host arithmetic, no device access; the
+// C-ABI layer calls it after validating the operands.
+#include "vrl_internal.h"
+
+#include <algorithm>
+#include <cstdint>
+
+namespace vrl {
+namespace {
+
+// n / d == (n * magic) >> shift for every n < 2^31 (see div_magic in the kernels).
+void magic_for(uint32_t d, uint64_t &magic, uint32_t &shift)
+{
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d)
+        ++l;
+    shift = 31 + l;
+    magic = ((uint64_t(1) << shift) + d - 1) / d;
+}
+
+// Largest vector width (bytes) that divides every address, stride and row.
+int vector_bytes(const PlanView *vs, int n, uintptr_t wire, int64_t D)
+{
+    uint64_t acc = uint64_t(D) * 2 | wire;
+    for (int i = 0; i < n; ++i) {
+        acc |= vs[i].ptr;
+        acc |= uint64_t(vs[i].st) * 2;
+        acc |= uint64_t(vs[i].sh) * 2;
+    }
+    for (int vb : {16, 8, 4})
+        if (acc % uint64_t(vb) == 0)
+            return vb;
+    return 2;
+}
+
+}  // namespace
+
+bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, uintptr_t wire,
+                 int32_t cb, int32_t ce, LaunchPlan &pl, const char **why)
+{
+    const Problem *d = &pb;
+    const int64_t G = d->H / d->P;
+    const int vb = vector_bytes(views, nviews, wire, d->D);
+    const int ve = vb / 2;
+
+    pl = LaunchPlan{};
+    pl.op = op;
+    pl.vec_bytes = vb;
+    // heads per wire row: the whole group, or one head chunk of it
+    const int64_t Gb = d->chunk_heads ? G / d->C : G;
+    pl.contig = true;
+    for (int i = 0; i < nviews; ++i)
+        if (Gb > 1 && views[i].sh != d->D)
+            pl.contig = false;
+
+    KernelArgs &a = pl.args;
+    for (int i = 0; i < 3; ++i) {
+        const PlanView &g = views[i < nviews ? i : 0];
+        a.view_ptr[i] = reinterpret_cast<uint16_t *>(g.ptr);
+        a.view_st[i] = g.st;
+        a.view_sh[i] = g.sh;
+    }
+    a.wire = reinterpret_cast<uint16_t *>(wire);
+    a.s_local = d->s_local;
+    a.P = d->P;
+    a.G = int32_t(G);
+    a.D = d->D;
+    a.C = d->C;
+    a.chunk_heads = d->chunk_heads;
+    a.row_heads = int32_t(Gb);
+
+    const int64_t chunk_q = d->s_local / d->C, chunk_r = d->s_local % d->C;
+    const int64_t row_vecs = Gb * d->D / ve;
+    const int64_t t_max = d->chunk_heads ? d->s_local : chunk_q + (chunk_r ? 1 : 0);
+    if (t_max > (int64_t(1) << 31) / row_vecs ||
+        t_max * row_vecs + int64_t(kTileVecs) >= (int64_t(1) << 31)) {
+        *why = "a chunk is too large (2^31 vectors or more); use more chunks";
+        return false;
+    }
+    const int64_t nvec_max = t_max * row_vecs;
+    a.chunk_q = int32_t(chunk_q);
+    a.chunk_r = int32_t(chunk_r);
+    a.c_begin = cb;
+    a.n_win = ce - cb;
+    a.row_vecs = uint32_t(row_vecs);
+    a.head_vecs = uint32_t(d->D / ve);
+    magic_for(a.row_vecs, a.row_magic, a.row_shift);
+    magic_for(a.head_vecs, a.head_magic, a.head_shift);
+    a.tiles = uint32_t((nvec_max + kTileVecs - 1) / kTileVecs);
+
+    // A view whose heads lie further apart than its tokens (head-major
+    // storage) makes the token and head axes swap for real.  Writing such a
+    // view row by row scatters 2*D-byte pieces over G heads; those calls go
+    // through the LDS-staged kernel, whose tiles hold TT tokens of all G heads
+    // and write each head's TT tokens as one run.  (Reading such a view
+    // piecewise costs little, so gathers stay direct unless VRL_STAGE_GATHER.)
+    bool head_major = false;
+    for (int i = 0; i < nviews; ++i)
+        if (views[i].sh > views[i].st)
+            head_major = true;
+    const bool gather = op == Op::Pack || op == Op::Split;
+    const int64_t row_bytes = Gb * d->D * 2;
+    const bool use_lds = VRL_SCATTER_MODE == 1 && row_bytes <= int64_t(kLdsBytes);
+    if (head_major && (!gather || VRL_STAGE_GATHER) && Gb > 1 &&
+        (use_lds || VRL_SCATTER_MODE == 2)) {
+        const int64_t tt = std::min<int64_t>(
+            {use_lds ? int64_t(kLdsBytes) / row_bytes : int64_t(VRL_VIEW_TOKENS), t_max, 4096});
+        pl.staged = true;
+        pl.lds_bytes = use_lds ? uint32_t(tt * row_bytes) : 0;
+        a.tile_tokens = uint32_t(tt);
+        magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
+        a.tiles = uint32_t((t_max + tt - 1) / tt);
+    }
+    const int64_t planes = (op == Op::Pack || op == Op::Unpack) ? 3 : 1;
+    const int64_t grid = int64_t(d->P) * (ce - cb) * planes * a.tiles;
+    if (grid >= (int64_t(1) << 31)) {
+        *why = "the launch needs 2^31 workgroups or more";
+        return false;
+    }
+    pl.grid = uint32_t(grid);
+    return true;
+}
+
+}  // namespace vrl

@@ -193,3 +193,12 @@ def test_head_chunk_validation(vrl_lib):
     assert [L.vrl_chunk_offset(_dh(2, 4, 27707, 56, 128), c) for c in range(5)] == [0, 7, 14, 21, 28]
     assert L.vrl_exchange_elems(0, _dh(2, 4, 27707, 56, 128)) == 3 * 27707 * 56 * 128
     assert L.vrl_exchange_elems(1, _dh(2, 3, 10, 8, 8)) == -1
+
+
+def test_views_reaching_absurdly_far_are_rejected(vrl_lib):
+    dims = (2, 4, 16, 4, 8)
+    q, k, v = fused_qkv(dims)
+    huge = V(BASE, 1 << 62, 8)
+    assert pack(vrl_lib, dims, huge, k, v) == INVALID
+    assert "2^48" in _lib.last_error()
+    assert pack(vrl_lib, dims, q, k, V(BASE, 96, 1 << 60)) == INVALID
