@@ -61,3 +61,18 @@ def test_config4_pad_sentinel_never_copied(gpu):
     vrl.qkv_pack(*dev_qkv(d, w.H, w.D), out, w.P, w.C)
     torch.cuda.synchronize()
     assert not bool((out.view(torch.int16) == datagen.PAD_SENTINEL).any())
+
+
+@pytest.mark.gpu
+def test_offsets_beyond_2_31_elements(gpu):
+    """Wire buffers of 2.2e9 elements (4.4 GB per rank): element offsets pass
+    2^31, so every address product must be 64-bit.  P=2, C=2, 90,000
+    tokens/rank, 64 heads of 128; the whole path against the oracle."""
+    from dataclasses import replace
+    w = replace(WORKLOADS[2], name="large offsets", s_local=90000, H=64, total_tokens=180000, C=2)
+    assert 3 * w.s_local * w.H * w.D > 2**31
+    say("[large] generating inputs")
+    fused = [datagen.fused_source(w, r) for r in range(w.P)]
+    run_pipeline(gpu, w.P, w.C, w.s_local, w.H, w.D, fused, "large", planes=(1,))
+    del fused
+    torch.cuda.empty_cache()
