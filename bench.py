@@ -47,10 +47,17 @@ KERNEL_SOURCES = ["head_relayout_amd/csrc/vrl_kernels.hip", "head_relayout_amd/c
 
 
 def kernel_source_hash() -> str:
+    """Hash of the code (comments and whitespace stripped) that decides the
+    kernels' memory traffic."""
+    import re
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,11 +4,13 @@
 // section "What is enabled": QKV destination pack, attention-result split,
 // returned-head merge; plus the receive-side QKV unpack named in the
 // performance guide's sequence-head profile) are one batched copy between a
-// dense wire block [T(c)][G][D] and a strided region of a caller's view:
+// dense wire block [T][Gb][D] and a strided region of a caller's view:
 //
-//   wire row (token t of the block)  <->  view row: G heads of D elements at
+//   wire row (token t of the block)  <->  view row: Gb heads of D elements at
 //                                         token tok0 + t, heads head0 ..
 //
+// With token chunks a block is T(c) tokens of all G heads of a group; with
+// head chunks it is all S_l tokens of Gc = G / C heads.
 // Pack and merge touch the [S_l][H][D] side (dest/source rank selects the
 // head group), unpack and split the [S][G][D] side (rank selects the token
 // range).  Pack and split gather view -> wire, unpack and merge scatter
@@ -26,6 +28,9 @@
 // dense wire offset of vector f is f itself; the view offset needs f's row
 // and column, obtained with a precomputed multiply-shift division.  Address
 // arithmetic is 64-bit wherever a product can pass 2^31 elements.
+//
+// Views stored head-major, written by a scatter, go through staged_kernel
+// instead: an LDS transpose that writes each head's tokens as one run.
 #include "vrl_internal.h"
 
 namespace vrl {
@@ -50,6 +55,12 @@ struct Vec<2> {
     typedef uint16_t type;
 };
 
+// Build-time knobs, kept so the measured alternatives can be rebuilt; the
+// defaults are the measured best at the representative shape.
+//   VRL_RANK_INNER   pack/merge workgroups rank-innermost (1) or outermost
+//   VRL_PLANE_INNER  pack workgroups plane-innermost after the rank
+//   VRL_CHUNK_INNER  head-chunked scatters chunk-innermost
+//   VRL_LOAD_NT / VRL_STORE_NT  non-temporal loads / stores
 #ifndef VRL_RANK_INNER
 #define VRL_RANK_INNER 1
 #endif
@@ -118,7 +129,7 @@ struct Traits<Op::Merge> {
 // tile of that block it moves; plus the block's token count and the base
 // pointers of its wire block and of its first view row.
 struct Block {
-    int64_t T;           // tokens in the chunk
+    int64_t T;           // tokens (wire rows) in the block
     uint32_t tile;
     uint32_t plane;
     int64_t st, sh;      // the view's strides for this plane
@@ -219,8 +230,8 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
 }
 
 // Direct kernel: each workgroup moves kTileVecs consecutive vectors of a
-// wire block; the view side follows.  Used whenever the view's heads are
-// not stored further apart than its tokens.
+// wire block; the view side follows.  Used for every call except scatters
+// into head-major views.
 template <Op OP, int VB, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 {
