@@ -1,0 +1,130 @@
+"""Seeded random parity sweep of all four relayouts against the oracle.
+
+Each case draws P, the head-group size, head_dim, tokens per rank, the chunk
+reading (tokens or heads) and count, a chunk window, padded source rows, a
+source base offset of 0-4 elements, and dense / padded / head-major layouts
+for the attention side and the merge output.  Every op writes into a
+sentinel-filled buffer (with guard bands); the whole buffer, untouched parts
+included, must equal the oracle's result on a buffer filled the same way.
+Values avoid the sentinel and NaN patterns; everything else is random bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import head_relayout_amd as vrl
+import oracle
+from tests.gpu_harness import SENTINEL, assert_bits_equal, assert_guard_intact, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 600
+
+
+def _layout(rng, rows, heads, D):
+    """(shape of a backing buffer, function mapping it to a [rows][heads][D] view)"""
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        return (rows, heads, D), lambda b: b
+    if kind == 1:
+        pad = int(rng.integers(1, 8))
+        return (rows, heads * D + pad), lambda b: b[:, :heads * D].reshape(rows, heads, D) \
+            if isinstance(b, np.ndarray) else b[:, :heads * D].unflatten(1, (heads, D))
+    return (heads, rows, D), lambda b: b.transpose(1, 0, 2) if isinstance(b, np.ndarray) else b.transpose(0, 1)
+
+
+def _sentinel(shape):
+    return np.full(shape, SENTINEL, dtype=np.uint16)
+
+
+def _dev_guarded(host, dev):
+    """A device copy of `host` inside an allocation with guard bands."""
+    flat = np.concatenate([_sentinel(2048), host.reshape(-1), _sentinel(2048)])
+    whole = to_dev(flat, dev)
+    return whole[2048:2048 + host.size].view(host.shape), whole
+
+
+def _case(rng):
+    P = int(rng.choice([1, 2, 3, 4, 8]))
+    G = int(rng.integers(1, 7))
+    H = P * G
+    D = int(rng.choice([2, 4, 6, 8, 16, 24, 64, 128]))
+    S_l = int(rng.integers(1, 41))
+    hc = bool(rng.integers(0, 2))
+    if hc:
+        C = int(rng.choice([c for c in range(1, G + 1) if G % c == 0]))
+    else:
+        C = int(rng.integers(1, min(S_l, 6) + 1))
+    cb = int(rng.integers(0, C))
+    ce = int(rng.integers(cb + 1, C + 1))
+    if rng.random() < 0.4:
+        cb, ce = 0, C
+    return dict(P=P, G=G, H=H, D=D, S_l=S_l, C=C, hc=hc, cb=cb, ce=ce,
+                pad=int(rng.choice([0, 0, 1, 2, 3, 8])), base=int(rng.choice([0, 0, 1, 2, 4])))
+
+
+def test_random_cases(gpu):
+    rng = np.random.default_rng(20261202)
+    for n in range(N_CASES):
+        k = _case(rng)
+        P, G, H, D, S_l, C, hc, cb, ce = (k[x] for x in ("P", "G", "H", "D", "S_l", "C", "hc", "cb", "ce"))
+        S = P * S_l
+        kw = dict(chunk_heads=hc)
+        tag = f"case {n}: {k}"
+        if n % 40 == 0:
+            say(f"[random] {tag}")
+        od = oracle.dims(P, C, S_l, H, D)
+        n_qkv = 3 * S_l * H * D
+        n_att = S_l * H * D
+
+        # pack: source rows with padding, device copy shifted by `base` elements
+        fused = rng.integers(0, 0x7F00, size=(S_l, 3 * H * D + k["pad"]), dtype=np.uint16)
+        hq = [fused[:, i * H * D:(i + 1) * H * D].reshape(S_l, H, D) for i in range(3)]
+        flat = to_dev(np.concatenate([np.zeros(k["base"], np.uint16), fused.reshape(-1)]), gpu)
+        dfused = flat[k["base"]:].view(fused.shape)
+        dq = [dfused[:, i * H * D:(i + 1) * H * D].unflatten(1, (H, D)) for i in range(3)]
+        want = _sentinel(n_qkv)
+        oracle.qkv_pack(od, *hq, want, cb, ce, **kw)
+        got, whole = _dev_guarded(_sentinel(n_qkv), gpu)
+        vrl.qkv_pack(*dq, got, P, C, cb, ce, **kw)
+        torch.cuda.synchronize()
+        assert_bits_equal(got, want, f"{tag} pack")
+        assert_guard_intact(whole, f"{tag} pack")
+
+        # unpack into random layouts
+        recv = rng.integers(0, 0x7F00, size=n_qkv, dtype=np.uint16)
+        drecv = to_dev(recv, gpu)
+        lays = [_layout(rng, S, G, D) for _ in range(3)]
+        hbufs = [_sentinel(shape) for shape, _ in lays]
+        oracle.qkv_unpack(od, recv, *[f(b) for b, (_, f) in zip(hbufs, lays)], cb, ce, **kw)
+        dev = [_dev_guarded(_sentinel(shape), gpu) for shape, _ in lays]
+        vrl.qkv_unpack(drecv, *[f(d[0]) for d, (_, f) in zip(dev, lays)], P, C, cb, ce, **kw)
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert_bits_equal(dev[i][0], hbufs[i], f"{tag} unpack plane {i}")
+            assert_guard_intact(dev[i][1], f"{tag} unpack plane {i}")
+
+        # split from a random layout (the first unpacked plane's buffer, fully
+        # overwritten with values first)
+        oshape, of = lays[0]
+        obuf = rng.integers(0, 0x7F00, size=oshape, dtype=np.uint16)
+        dobuf = to_dev(obuf, gpu)
+        want = _sentinel(n_att)
+        oracle.attn_split(od, of(obuf), want, cb, ce, **kw)
+        got, whole = _dev_guarded(_sentinel(n_att), gpu)
+        vrl.attn_split(of(dobuf), got, P, C, cb, ce, **kw)
+        torch.cuda.synchronize()
+        assert_bits_equal(got, want, f"{tag} split")
+        assert_guard_intact(whole, f"{tag} split")
+
+        # merge into a random layout
+        back = rng.integers(0, 0x7F00, size=n_att, dtype=np.uint16)
+        mshape, mf = _layout(rng, S_l, H, D)
+        hm = _sentinel(mshape)
+        oracle.head_merge(od, back, mf(hm), cb, ce, **kw)
+        dm, whole = _dev_guarded(_sentinel(mshape), gpu)
+        vrl.head_merge(to_dev(back, gpu), mf(dm), P, C, cb, ce, **kw)
+        torch.cuda.synchronize()
+        assert_bits_equal(dm, hm, f"{tag} merge")
+        assert_guard_intact(whole, f"{tag} merge")
+    say(f"[random] {N_CASES} cases ok")
