@@ -787,16 +787,26 @@ def trace_summary(d):
             key = (r["Kernel_Name"], int(r["Grid_Size_X"]))
             groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     print(f"# kernel sources: sha256 prefix {kernel_source_hash()}")
+    print("# GB/s only for whole-tensor launches (the largest grid of a kernel); smaller grids")
+    print("# are chunk-window launches (the overlap schedule, the one-chunk split).")
     print(f"{'kernel':<36} {'grid':>9} {'calls':>5} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"
           f" {'GB/s(avg)':>10} {'%8TB/s':>7}")
+    full = {}
+    for (name, grid) in groups:
+        full[name] = max(full.get(name, 0), grid)
     for (name, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         avg = sum(ns) / len(ns)
         cols = f"{grid:>9} {len(ns):>5} {avg / 1e3:9.1f} {min(ns) / 1e3:9.1f} {max(ns) / 1e3:9.1f}"
         if "(vrl::Op)" in name:
             op = names[name.split("(vrl::Op)")[1][0]]
             kind = "staged" if "staged_kernel" in name else "direct"
-            gbs = nb[op] / (avg * 1e-9) / 1e9
-            print(f"{kind + ' ' + op:<36} {cols} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")
+            if kind == "direct" and name.rstrip().endswith("false>(vrl::KernelArgs)"):
+                kind = "direct strided-heads"
+            if grid == full[name]:
+                gbs = nb[op] / (avg * 1e-9) / 1e9
+                print(f"{kind + ' ' + op:<36} {cols} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")
+            else:
+                print(f"{kind + ' ' + op + ' (window)':<36} {cols} {'-':>10} {'-':>7}")
         elif "copyBuffer" in name:
             print(f"{'__amd_rocclr_copyBuffer (exchanges)':<36} {cols}")
 
