@@ -274,6 +274,9 @@ def run_bench(args):
         result["head_chunks"] = head_chunk_layout(torch, vrl, w, ranks)
         say("[bench] head-major (BHTD) attention side")
         result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
+        if w.cid == 3:
+            say("[bench] padded source rows (row stride 21,568)")
+            result["strided_rows"] = strided_rows(torch, np, datagen, vrl, dev)
     if not args.no_reference and not args.no_extras:
         say("[bench] reference materialisation arm (A/direct/A)")
         result["reference_arm"] = reference_arm(torch, vrl, w, ranks[0])
@@ -581,6 +584,46 @@ def head_major_layouts(torch, vrl, w, rk):
             raise SystemExit("head-major unpack differs from token-major unpack")
     if not torch.equal(send.view(torch.int16), rk.send.view(torch.int16)):
         raise SystemExit("split from head-major O differs from split from token-major O")
+    return out
+
+
+def strided_rows(torch, np, datagen, vrl, dev):
+    """The representative shape with every token row of the fused QKV source
+    padded to 21,568 elements (Q/K/V at column offsets 0 / 7,168 / 14,336, 64
+    sentinel pad columns): pack from those rows, and merge both into a dense
+    [S_l][H][D] output and into rows of the same padded stride.  The round
+    trip must return Q bit for bit and leave the pad columns untouched."""
+    w = datagen.WORKLOADS[4]
+    P, C, S_l, H, D = w.P, w.C, w.s_local, w.H, w.D
+    ranks = [Rank(w, r, dev, torch, np, datagen, vrl) for r in range(P)]
+    for rk in ranks:
+        vrl.qkv_pack(*rk.qkv, rk.packed, P, C)
+    exchange([rk.packed for rk in ranks], [rk.recv for rk in ranks], P)
+    for rk in ranks:
+        vrl.qkv_unpack(rk.recv, *rk.planes, P, C)
+        vrl.attn_split(rk.planes[0], rk.send, P, C)
+    exchange([rk.send for rk in ranks], [rk.back for rk in ranks], P)
+    rk = ranks[0]
+    row = rk.fused.shape[1]
+    padded = torch.full((S_l, row), datagen.PAD_SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    padded_view = padded[:, :H * D].unflatten(1, (H, D))
+    nb = op_bytes(w)
+    out = {"row_stride_elems": row}
+    for name, fn, nbytes in (
+            ("qkv_pack", lambda: vrl.qkv_pack(*rk.qkv, rk.packed, P, C), nb["qkv_pack"]),
+            ("head_merge", lambda: vrl.head_merge(rk.back, rk.merged, P, C), nb["head_merge"]),
+            ("head_merge_padded_rows", lambda: vrl.head_merge(rk.back, padded_view, P, C),
+             nb["head_merge"])):
+        ms = _median_ms(torch, fn)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+    torch.cuda.synchronize()
+    q = rk.qkv[0].reshape(S_l, H * D).view(torch.int16)
+    if not (torch.equal(rk.merged.view(S_l, H * D).view(torch.int16), q)
+            and torch.equal(padded[:, :H * D].view(torch.int16), q)):
+        raise SystemExit("padded-row round trip is not bit-exact")
+    if not bool((padded[:, H * D:].view(torch.int16) == datagen.PAD_SENTINEL).all()):
+        raise SystemExit("merge into padded rows touched the pad columns")
     return out
 
 
