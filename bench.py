@@ -19,9 +19,11 @@ dominant kernel (QKV pack) against the 8 TB/s HBM3E peak, a device-to-device
 copy of the pack's size for comparison, and the CPU oracle timed on the
 host's cores on a bounded sample (rank 0's four chains once).
 
-Other modes: --mode pmc runs only QKV pack (rank 0) and a plain torch copy
-kernel of known size, for rocprofv3 counter runs; --pmc-summary turns the
-counter CSVs of those runs into the traffic figures kept under profiles/.
+Other modes: --mode pmc launches each relayout kernel the representative
+shape uses, token-major and head-major layouts (rank 0), and a plain torch
+copy kernel of known size, for rocprofv3 counter runs; --pmc-summary turns
+the counter CSVs of those runs into the traffic figures kept under
+profiles/.
 """
 from __future__ import annotations
 
@@ -40,7 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "QKV-pack / head-merge ms and effective HBM GB/s (% of peak) at 55,413 tokens"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_pack_repr55413_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "relayout_kernels_repr55413_traffic.txt")
 # what decides the kernels' memory traffic: device code and launch planning
 KERNEL_SOURCES = ["head_relayout_amd/csrc/vrl_kernels.hip", "head_relayout_amd/csrc/vrl_internal.h",
                   "head_relayout_amd/csrc/vrl_plan.cpp"]
@@ -695,8 +697,38 @@ def read_traffic():
 
 # ---- counter runs --------------------------------------------------------------
 
+# Kernels of the counter runs, in launch order: (label, op, kind).  Each is a
+# distinct kernel instantiation, so per-kernel rows of a counter CSV map back
+# to these labels.
+PMC_KERNELS = [
+    ("qkv_pack", "qkv_pack", "direct"),
+    ("qkv_unpack", "qkv_unpack", "direct"),
+    ("attn_split", "attn_split", "direct"),
+    ("head_merge", "head_merge", "direct"),
+    ("qkv_unpack head-major", "qkv_unpack", "staged"),
+    ("head_merge head-major", "head_merge", "staged"),
+    ("attn_split head-major", "attn_split", "direct strided-heads"),
+]
+
+
+def kernel_label(name):
+    """(op, kind) of a relayout kernel's mangled-and-demangled name, or None."""
+    if "(vrl::Op)" not in name:
+        return None
+    op = {"0": "qkv_pack", "1": "qkv_unpack", "2": "attn_split",
+          "3": "head_merge"}[name.split("(vrl::Op)")[1][0]]
+    if "staged_kernel" in name:
+        return op, "staged"
+    if name.rstrip().endswith("false>(vrl::KernelArgs)"):
+        return op, "direct strided-heads"
+    return op, "direct"
+
+
 def run_pmc(args):
-    """QKV pack of rank 0 and a plain copy kernel, `reps` launches each."""
+    """Every relayout kernel the representative shape uses (the four
+    token-major ones, the staged scatters into head-major views and the split
+    from a head-major view) on rank 0's buffers, and a plain copy kernel,
+    `reps` launches each."""
     import numpy as np
     import torch
 
@@ -705,17 +737,34 @@ def run_pmc(args):
 
     dev = torch.device("cuda:0")
     w = datagen.WORKLOADS[args.workload]
+    P, C = w.P, w.C
     rk = Rank(w, 0, dev, torch, np, datagen, vrl)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    vrl.qkv_pack(*rk.qkv, rk.packed, P, C)
+    rk.recv.copy_(rk.packed)
+    rk.back.copy_(rk.packed[:rk.back.numel()])
+    hm = [torch.empty(w.G, w.S, w.D, **bf).transpose(0, 1) for _ in range(3)]
+    merged_hm = torch.empty(w.H, w.s_local, w.D, **bf).transpose(0, 1)
+    launches = {
+        "qkv_pack": lambda: vrl.qkv_pack(*rk.qkv, rk.packed, P, C),
+        "qkv_unpack": lambda: vrl.qkv_unpack(rk.recv, *rk.planes, P, C),
+        "attn_split": lambda: vrl.attn_split(rk.planes[0], rk.send, P, C),
+        "head_merge": lambda: vrl.head_merge(rk.back, rk.merged, P, C),
+        "qkv_unpack head-major": lambda: vrl.qkv_unpack(rk.recv, *hm, P, C),
+        "head_merge head-major": lambda: vrl.head_merge(rk.back, merged_hm, P, C),
+        "attn_split head-major": lambda: vrl.attn_split(hm[0], rk.send, P, C),
+    }
     n = rk.packed.numel()
     a = torch.zeros(n, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
-    for _ in range(args.reps):
-        vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
+    for label, _, _ in PMC_KERNELS:
+        for _ in range(args.reps):
+            launches[label]()
     for _ in range(args.reps):
         torch.bitwise_not(a, out=b)     # reads n*2 bytes, writes n*2 bytes
     torch.cuda.synchronize()
-    print(f"pmc: {args.reps} x qkv_pack ({op_bytes(w)['qkv_pack'] // 2} B read + written), "
-          f"{args.reps} x bitwise_not copy kernel ({2 * n} B read + written)", flush=True)
+    print(f"pmc: {args.reps} launches each of {len(PMC_KERNELS)} relayout kernels and of a "
+          f"bitwise_not copy kernel ({2 * n} B read + written)", flush=True)
 
 
 def run_pmc_lds(args):
@@ -748,13 +797,10 @@ def sq_summary(d):
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             for r in csv.DictReader(f):
-                name = r["Kernel_Name"]
-                if "(vrl::Op)" not in name:
+                lab = kernel_label(r["Kernel_Name"])
+                if lab is None:
                     continue
-                op = {"0": "qkv_pack", "1": "qkv_unpack", "2": "attn_split",
-                      "3": "head_merge"}[name.split("(vrl::Op)")[1][0]]
-                kind = "staged" if "staged_kernel" in name else "direct"
-                rows.setdefault((kind + " " + op, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                rows.setdefault((lab[1] + " " + lab[0], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     kernels = sorted({k for k, _ in rows})
     counters = sorted({c for _, c in rows})
     print(f"{'kernel':<22}" + "".join(f"{c:>24}" for c in counters))
@@ -764,8 +810,10 @@ def sq_summary(d):
 
 
 def pmc_summary(fetch_dir, write_dir):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the pack kernel and of
-    the copy kernel; the copy kernel's known size calibrates the counters."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every relayout kernel of
+    a --mode pmc run and of the copy kernel; the copy kernel's known size
+    calibrates the counters.  The first two lines (source hash, pack bytes
+    per launch) are what the benchmark's roofline reads."""
     def load(d, counter):
         rows = {}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -773,43 +821,49 @@ def pmc_summary(fetch_dir, write_dir):
                 for row in csv.DictReader(f):
                     if row.get("Counter_Name") != counter:
                         continue
-                    name = row["Kernel_Name"]
-                    rows.setdefault(name, []).append(float(row["Counter_Value"]))
+                    rows.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
         return rows
 
     fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
 
-    def pick(rows, key):
-        ks = [k for k in rows if key in k]
-        if not ks:
-            raise SystemExit(f"no kernel matching {key!r} in {sorted(rows)}")
+    def mean_of(rows, match):
+        ks = [k for k in rows if match(k)]
+        if len(ks) != 1:
+            raise SystemExit(f"expected one kernel, found {ks} in {sorted(rows)}")
         vals = rows[ks[0]]
         return ks[0], sum(vals) / len(vals), len(vals)
 
     import datagen
     w = datagen.WORKLOADS[3]
-    pack_bytes = op_bytes(w)["qkv_pack"] // 2           # read (= written) bytes per launch
+    nb = op_bytes(w)
     copy_bytes = 3 * w.s_local * w.H * w.D * 2
-    kp, pf, npf = pick(fetch, "relayout_kernel")
-    kc, cf, ncf = pick(fetch, "bitwise_not")
-    _, pw, npw = pick(write, "relayout_kernel")
-    _, cw, ncw = pick(write, "bitwise_not")
+    kc, cf, ncf = mean_of(fetch, lambda k: "bitwise_not" in k)
+    _, cw, ncw = mean_of(write, lambda k: "bitwise_not" in k)
     f_scale = copy_bytes / (cf * 1024)
     w_scale = copy_bytes / (cw * 1024)
-    pack_fetch = pf * 1024 * f_scale
-    pack_write = pw * 1024 * w_scale
+    table, pack_total = [], None
+    for label, op, kind in PMC_KERNELS:
+        def match(k, op=op, kind=kind):
+            return kernel_label(k) == (op, kind)
+        kname, f, nf = mean_of(fetch, match)
+        _, wr, nw = mean_of(write, match)
+        fb, wb = f * 1024 * f_scale, wr * 1024 * w_scale
+        half = nb[op] // 2
+        if label == "qkv_pack":
+            pack_total = int(round(fb + wb))
+        table.append(f"# {label:<24} {half:>14} {fb:>16.0f} {wb:>16.0f} {fb / half:>8.4f} {wb / half:>8.4f}"
+                     f"   {nf}/{nw}")
     lines = [
         f"kernel_source_sha256 {kernel_source_hash()}",
-        f"hbm_bytes_per_launch {int(round(pack_fetch + pack_write))}",
-        f"# pack kernel: {kp}",
-        f"#   FETCH_SIZE {pf:.1f} KiB/dispatch over {npf} dispatches, WRITE_SIZE {pw:.1f} KiB/dispatch over {npw}",
+        f"hbm_bytes_per_launch {pack_total}",
         f"# copy kernel: {kc}",
         f"#   FETCH_SIZE {cf:.1f} KiB/dispatch over {ncf}, WRITE_SIZE {cw:.1f} KiB/dispatch over {ncw}",
         f"#   known size {copy_bytes} B read and {copy_bytes} B written per dispatch",
         f"#   calibration: fetch x{f_scale:.4f}, write x{w_scale:.4f}",
-        f"# pack per launch: fetched {pack_fetch:.0f} B, written {pack_write:.0f} B;"
-        f" algorithmic {pack_bytes} B each way ({pack_fetch / pack_bytes:.4f}x, {pack_write / pack_bytes:.4f}x)",
-    ]
+        "# per launch, calibrated; algorithmic = bytes read = bytes written",
+        f"# {'kernel':<24} {'algorithmic B':>14} {'fetched B':>16} {'written B':>16} {'fetch/x':>8} "
+        f"{'write/x':>8}   dispatches",
+    ] + table
     print("\n".join(lines))
 
 
@@ -820,7 +874,6 @@ def trace_summary(d):
 
     w = datagen.WORKLOADS[3]
     nb = op_bytes(w)
-    names = {"0": "qkv_pack", "1": "qkv_unpack", "2": "attn_split", "3": "head_merge"}
     paths = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_trace.csv under {d}")
@@ -840,11 +893,8 @@ def trace_summary(d):
     for (name, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         avg = sum(ns) / len(ns)
         cols = f"{grid:>9} {len(ns):>5} {avg / 1e3:9.1f} {min(ns) / 1e3:9.1f} {max(ns) / 1e3:9.1f}"
-        if "(vrl::Op)" in name:
-            op = names[name.split("(vrl::Op)")[1][0]]
-            kind = "staged" if "staged_kernel" in name else "direct"
-            if kind == "direct" and name.rstrip().endswith("false>(vrl::KernelArgs)"):
-                kind = "direct strided-heads"
+        if kernel_label(name) is not None:
+            op, kind = kernel_label(name)
             if grid == full[name]:
                 gbs = nb[op] / (avg * 1e-9) / 1e9
                 print(f"{kind + ' ' + op:<36} {cols} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")

@@ -34,3 +34,49 @@ def test_cpu_baseline_on_the_tiny_workload():
     assert out["kind"] == "oracle" and out["unit"] == "GB/s" and out["value"] > 0
     assert out["cores"] >= 1
     json.dumps(out)
+
+
+def _counter_csv(path, counter, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, value) in enumerate(rows):
+            f.write(f'{i},"{name}",{counter},{value}\n')
+
+
+def test_pmc_summary_maps_every_kernel_and_calibrates(tmp_path, capsys):
+    """Synthetic counter CSVs: FETCH_SIZE reading half the bytes, WRITE_SIZE
+    all of them, one kernel per label; the summary must scale both back to
+    exactly 1.0x of the algorithmic bytes and name the pack's total."""
+    import bench
+    import datagen
+
+    w = datagen.WORKLOADS[3]
+    nb = bench.op_bytes(w)
+    copy_kib = 3 * w.s_local * w.H * w.D * 2 / 1024
+    names = {
+        ("qkv_pack", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)0, 16, true>(vrl::KernelArgs)",
+        ("qkv_unpack", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)1, 16, true>(vrl::KernelArgs)",
+        ("attn_split", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)2, 16, true>(vrl::KernelArgs)",
+        ("head_merge", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)3, 16, true>(vrl::KernelArgs)",
+        ("qkv_unpack", "staged"): "void vrl::(anonymous namespace)::staged_kernel<(vrl::Op)1, 16, true>(vrl::KernelArgs)",
+        ("head_merge", "staged"): "void vrl::(anonymous namespace)::staged_kernel<(vrl::Op)3, 16, true>(vrl::KernelArgs)",
+        ("attn_split", "direct strided-heads"):
+            "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)2, 16, false>(vrl::KernelArgs)",
+    }
+    for key, name in names.items():
+        assert bench.kernel_label(name) == key
+    copy = "void at::native::elementwise_kernel<bitwise_not_kernel>(int, Op)"
+    fetch = [(names[(op, kind)], nb[op] / 2 / 1024 / 2) for _, op, kind in bench.PMC_KERNELS]
+    write = [(names[(op, kind)], nb[op] / 2 / 1024) for _, op, kind in bench.PMC_KERNELS]
+    _counter_csv(str(tmp_path / "f" / "x_counter_collection.csv"), "FETCH_SIZE", fetch + [(copy, copy_kib / 2)])
+    _counter_csv(str(tmp_path / "w" / "x_counter_collection.csv"), "WRITE_SIZE", write + [(copy, copy_kib)])
+    bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"))
+    out = capsys.readouterr().out.splitlines()
+    assert out[0] == f"kernel_source_sha256 {bench.kernel_source_hash()}"
+    assert out[1] == f"hbm_bytes_per_launch {nb['qkv_pack']}"
+    rows = [l for l in out if l.startswith("# ") and l.split()[1] in {"qkv_pack", "qkv_unpack", "attn_split",
+                                                                        "head_merge"}]
+    assert len(rows) == len(bench.PMC_KERNELS)
+    for r in rows:
+        assert r.split()[-3:-1] == ["1.0000", "1.0000"], r
