@@ -54,6 +54,10 @@ SHAPES = [
     (2, 3, 11, 4, 128, 8),    # 16-byte vectors, padded rows
     (2, 2, 9, 2, 200, 0),     # head_dim not a power of two, one head per group
     (2, 7, 40, 6, 24, 0),     # 3 heads per group of 24
+    (2, 2, 6, 4, 1, 0),       # head_dim 1: one element per head row
+    (3, 2, 7, 6, 3, 1),       # odd head_dim, padded rows
+    (2, 3, 8, 4, 5, 0),       # odd head_dim, 2-byte vectors throughout
+    (2, 2, 4, 4, 256, 0),     # head_dim 256
 ]
 IDS = [f"P{s[0]}C{s[1]}S{s[2]}H{s[3]}D{s[4]}pad{s[5]}" for s in SHAPES]
 
@@ -189,3 +193,15 @@ def test_split_config5_attention_output(gpu, head_major):
         torch.cuda.synchronize()
         assert_bits_equal(send, ref, f"cfg5 split rank {r} head_major={head_major}")
         assert_guard_intact(whole, "cfg5 split")
+
+
+@pytest.mark.parametrize("layout", ["dense", "head_major"])
+def test_rows_wider_than_the_lds_tile(gpu, layout):
+    """A head group wider than the staged kernel's 16 KiB LDS tile (66 heads of
+    128: 16,896-byte rows): head-major scatters then run the direct kernel.
+    Random payloads (the shape has more elements than unique 16-bit ids)."""
+    P, C, S_l, H, D = 2, 2, 5, 132, 128
+    rng = np.random.default_rng(66)
+    fused = [rng.integers(0, 0x7F00, size=(S_l, 3 * H * D), dtype=np.uint16) for _ in range(P)]
+    lay = {"dense": {}, "head_major": {"head_major": True}}[layout]
+    run_pipeline(gpu, P, C, S_l, H, D, fused, f"wide-rows-{layout}", unpack_layout=lay, merge_layout=lay)
