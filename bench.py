@@ -279,6 +279,8 @@ def run_bench(args):
         if w.cid == 3:
             say("[bench] padded source rows (row stride 21,568)")
             result["strided_rows"] = strided_rows(torch, np, datagen, vrl, dev)
+            say("[bench] mid-size and P=4 workloads (buffer rotation past the Infinity Cache)")
+            result["smaller_workloads"] = smaller_workloads(torch, np, datagen, vrl, dev)
     if not args.no_reference and not args.no_extras:
         say("[bench] reference materialisation arm (A/direct/A)")
         result["reference_arm"] = reference_arm(torch, vrl, w, ranks[0])
@@ -626,6 +628,69 @@ def strided_rows(torch, np, datagen, vrl, dev):
         raise SystemExit("padded-row round trip is not bit-exact")
     if not bool((padded[:, H * D:].view(torch.int16) == datagen.PAD_SENTINEL).all()):
         raise SystemExit("merge into padded rows touched the pad columns")
+    return out
+
+
+def smaller_workloads(torch, np, datagen, vrl, dev, wids=(2, 5), reps=12):
+    """The four relayouts at the mid-size (P=2, 4,096 tokens/rank, 32 heads)
+    and P=4 (7,752 tokens/rank, 32 heads) workloads, rank 0's share.  Their
+    working sets fit the 256 MB Infinity Cache, so each op rotates over k
+    copies of its buffers with k x bytes per launch >= 1 GiB: every launch
+    reads inputs that the previous launches have evicted."""
+    out = {}
+    for wid in wids:
+        w = datagen.WORKLOADS[wid]
+        P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+        nb = op_bytes(w)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        host = datagen.fused_source(w, 0)
+        fused0 = torch.from_numpy(host.view(np.int16)).to(dev).view(torch.bfloat16)
+        k_big = -(-(1 << 30) // nb["qkv_pack"])
+        k_small = -(-(1 << 30) // nb["head_merge"])
+        sets = []
+        for i in range(max(k_big, k_small)):
+            fused = fused0.clone()
+            packed = torch.empty(3 * S_l * H * D, **bf)
+            vrl.qkv_pack(*[fused[:, j * H * D:(j + 1) * H * D].unflatten(1, (H, D)) for j in range(3)],
+                         packed, P, C)
+            sets.append({"qkv": [fused[:, j * H * D:(j + 1) * H * D].unflatten(1, (H, D)) for j in range(3)],
+                         "packed": packed, "planes": [torch.empty(S, G, D, **bf) for _ in range(3)],
+                         "send": torch.empty(S_l * H * D, **bf), "merged": torch.empty(S_l, H, D, **bf)})
+        for st in sets:      # stand-ins for the received buffers, and a filled O
+            vrl.qkv_unpack(st["packed"], *st["planes"], P, C)
+        ops = {
+            "qkv_pack": (k_big, lambda st: vrl.qkv_pack(*st["qkv"], st["packed"], P, C)),
+            "qkv_unpack": (k_big, lambda st: vrl.qkv_unpack(st["packed"], *st["planes"], P, C)),
+            "attn_split": (k_small, lambda st: vrl.attn_split(st["planes"][0], st["send"], P, C)),
+            "head_merge": (k_small, lambda st: vrl.head_merge(st["send"], st["merged"], P, C)),
+        }
+        res = {"P": P, "C": C, "s_local": S_l, "H": H, "D": D}
+        for name, (k, fn) in ops.items():
+            for i in range(k):
+                fn(sets[i])
+            pairs = []
+            for i in range(reps * k):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(sets[i % k])
+                e1.record()
+                pairs.append((e0, e1))
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in pairs)
+            ms = ts[len(ts) // 2]
+            gbs = nb[name] / (ms * 1e-3) / 1e9
+            res[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                         "buffer_sets": k, "launches": len(ts)}
+        # the rotation must not have changed what the ops compute
+        ref = sets[0]
+        for st in sets[1:]:
+            if not (torch.equal(st["packed"].view(torch.int16), ref["packed"].view(torch.int16))
+                    and torch.equal(st["merged"].view(torch.int16), ref["merged"].view(torch.int16))):
+                raise SystemExit(f"workload {wid}: buffer sets disagree")
+        if not torch.equal(ref["merged"].view(torch.int16), ref["qkv"][0].view(torch.int16)):
+            raise SystemExit(f"workload {wid}: round trip is not bit-exact")
+        out[w.name] = res
+        del sets
     return out
 
 
