@@ -932,13 +932,34 @@ def pmc_summary(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+def whole_tensor_grids():
+    """{(op, kind, grid in threads): (workload suffix, algorithmic bytes)} for
+    the whole-tensor launches of the workloads this benchmark runs.  It
+    follows the launch planner's tiling at 16-byte vectors: 256-lane
+    workgroups, 2,048 vectors per direct tile, staged tiles of as many whole
+    token rows as fit 16 KiB."""
+    import datagen
+
+    out = {}
+    for wid, suffix in ((3, ""), (2, " (mid-size)"), (5, " (P=4)")):
+        w = datagen.WORKLOADS[wid]
+        nb = op_bytes(w)
+        t_max = -(-w.s_local // w.C)
+        row_vecs = w.G * w.D // 8
+        tt = min(16384 // (w.G * w.D * 2), t_max)
+        for op, nbytes in nb.items():
+            blocks = w.P * w.C * (3 if op in ("qkv_pack", "qkv_unpack") else 1)
+            direct = 256 * blocks * -(-t_max * row_vecs // 2048)
+            out[(op, "direct", direct)] = (suffix, nbytes)
+            out[(op, "direct strided-heads", direct)] = (suffix, nbytes)
+            if tt >= 1:
+                out[(op, "staged", 256 * blocks * -(-t_max // tt))] = (suffix, nbytes)
+    return out
+
+
 def trace_summary(d):
     """Per-kernel table of a rocprofv3 --kernel-trace run of this benchmark,
     one row per (kernel, grid size)."""
-    import datagen
-
-    w = datagen.WORKLOADS[3]
-    nb = op_bytes(w)
     paths = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_trace.csv under {d}")
@@ -947,26 +968,26 @@ def trace_summary(d):
         for r in csv.DictReader(f):
             key = (r["Kernel_Name"], int(r["Grid_Size_X"]))
             groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    whole = whole_tensor_grids()
     print(f"# kernel sources: sha256 prefix {kernel_source_hash()}")
-    print("# GB/s only for whole-tensor launches (the largest grid of a kernel); smaller grids")
-    print("# are chunk-window launches (the overlap schedule, the one-chunk split).")
-    print(f"{'kernel':<36} {'grid':>9} {'calls':>5} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"
+    print("# GB/s for whole-tensor launches (representative shape unless the label names")
+    print("# another workload); \"(window)\" rows are chunk-window launches (the overlap")
+    print("# schedule, the one-chunk split).")
+    print(f"{'kernel':<40} {'grid':>9} {'calls':>5} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"
           f" {'GB/s(avg)':>10} {'%8TB/s':>7}")
-    full = {}
-    for (name, grid) in groups:
-        full[name] = max(full.get(name, 0), grid)
     for (name, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         avg = sum(ns) / len(ns)
         cols = f"{grid:>9} {len(ns):>5} {avg / 1e3:9.1f} {min(ns) / 1e3:9.1f} {max(ns) / 1e3:9.1f}"
         if kernel_label(name) is not None:
             op, kind = kernel_label(name)
-            if grid == full[name]:
-                gbs = nb[op] / (avg * 1e-9) / 1e9
-                print(f"{kind + ' ' + op:<36} {cols} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")
+            if (op, kind, grid) in whole:
+                suffix, nbytes = whole[(op, kind, grid)]
+                gbs = nbytes / (avg * 1e-9) / 1e9
+                print(f"{kind + ' ' + op + suffix:<40} {cols} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")
             else:
-                print(f"{kind + ' ' + op + ' (window)':<36} {cols} {'-':>10} {'-':>7}")
+                print(f"{kind + ' ' + op + ' (window)':<40} {cols} {'-':>10} {'-':>7}")
         elif "copyBuffer" in name:
-            print(f"{'__amd_rocclr_copyBuffer (exchanges)':<36} {cols}")
+            print(f"{'__amd_rocclr_copyBuffer (exchanges)':<40} {cols}")
 
 
 def main():

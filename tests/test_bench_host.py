@@ -80,3 +80,31 @@ def test_pmc_summary_maps_every_kernel_and_calibrates(tmp_path, capsys):
     assert len(rows) == len(bench.PMC_KERNELS)
     for r in rows:
         assert r.split()[-3:-1] == ["1.0000", "1.0000"], r
+
+
+def test_trace_summary_labels_workloads_and_windows(tmp_path, capsys):
+    """Synthetic kernel trace: whole-tensor launches of the representative and
+    P=4 shapes get GB/s from their own algorithmic bytes; a one-chunk window
+    launch gets none."""
+    import bench
+
+    pack = "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)0, 16, true>(vrl::KernelArgs)"
+    rows = [(pack, 9314304, 400_000), (pack, 9314304, 400_000),   # representative: 400 us
+            (pack, 1499136, 66_000),                               # P=4 whole tensor
+            (pack, 2328576, 100_000),                              # one chunk of the representative
+            ("__amd_rocclr_copyBuffer", 131072, 50_000)]
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "x_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Grid_Size_X,Start_Timestamp,End_Timestamp\n")
+        for name, grid, ns in rows:
+            f.write(f'"{name}",{grid},1000,{1000 + ns}\n')
+    bench.trace_summary(str(d))
+    out = capsys.readouterr().out.splitlines()
+    rep = [l for l in out if l.startswith("direct qkv_pack ") and " 9314304 " in l]
+    assert len(rep) == 1 and rep[0].split()[-2:] == ["5958", "74.5"], rep   # 2,383,245,312 B / 400 us
+    p4 = [l for l in out if l.startswith("direct qkv_pack (P=4)")]
+    assert len(p4) == 1 and p4[0].split()[-2:] == ["5773", "72.2"], p4     # 381,026,304 B / 66 us
+    win = [l for l in out if l.startswith("direct qkv_pack (window)")]
+    assert len(win) == 1 and win[0].split()[-2:] == ["-", "-"]
+    assert any(l.startswith("__amd_rocclr_copyBuffer") for l in out)
