@@ -16,8 +16,9 @@ Printed: one JSON line with the whole step's effective HBM throughput
 (algorithmic bytes: every element read once and written once), per-op
 times from HIP events recorded on the launch stream, the roofline of the
 dominant kernel (QKV pack) against the 8 TB/s HBM3E peak, a device-to-device
-copy of the pack's size for comparison, and the CPU oracle timed on the
-host's cores on a bounded sample (rank 0's four chains once).
+copy of the pack's size for comparison, sections for the other layouts and
+workloads (untimed by the step), and the CPU oracle timed on the host's
+cores over one step of the workload (median of five passes).
 
 Other modes: --mode pmc launches each relayout kernel the representative
 shape uses, token-major and head-major layouts (rank 0), and a plain torch
