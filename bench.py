@@ -80,7 +80,7 @@ def parse_args():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed step: skip the overlap, head-chunk, head-major and "
                          "reference sections (for profiler runs)")
-    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-lds"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-sq"], default="bench")
     ap.add_argument("--reps", type=int, default=10, help="launches per kernel in --mode pmc")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output trees (FETCH_SIZE, WRITE_SIZE)")
@@ -771,8 +771,8 @@ PMC_KERNELS = [
     ("qkv_unpack", "qkv_unpack", "direct"),
     ("attn_split", "attn_split", "direct"),
     ("head_merge", "head_merge", "direct"),
-    ("qkv_unpack head-major", "qkv_unpack", "staged"),
-    ("head_merge head-major", "head_merge", "staged"),
+    ("qkv_unpack head-major", "qkv_unpack", "head-run"),
+    ("head_merge head-major", "head_merge", "head-run"),
     ("attn_split head-major", "attn_split", "direct strided-heads"),
 ]
 
@@ -783,8 +783,8 @@ def kernel_label(name):
         return None
     op = {"0": "qkv_pack", "1": "qkv_unpack", "2": "attn_split",
           "3": "head_merge"}[name.split("(vrl::Op)")[1][0]]
-    if "staged_kernel" in name:
-        return op, "staged"
+    if "headrun_kernel" in name:
+        return op, "head-run"
     if name.rstrip().endswith("false>(vrl::KernelArgs)"):
         return op, "direct strided-heads"
     return op, "direct"
@@ -792,7 +792,7 @@ def kernel_label(name):
 
 def run_pmc(args):
     """Every relayout kernel the representative shape uses (the four
-    token-major ones, the staged scatters into head-major views and the split
+    token-major ones, the head-run scatters into head-major views and the split
     from a head-major view) on rank 0's buffers, and a plain copy kernel,
     `reps` launches each."""
     import numpy as np
@@ -833,8 +833,8 @@ def run_pmc(args):
           f"bitwise_not copy kernel ({2 * n} B read + written)", flush=True)
 
 
-def run_pmc_lds(args):
-    """The staged (LDS) unpack into head-major Q/K/V, the direct unpack into
+def run_pmc_sq(args):
+    """The head-run unpack into head-major Q/K/V, the direct unpack into
     token-major ones and the pack, `reps` launches each, for SQ counter runs."""
     import numpy as np
     import torch
@@ -845,6 +845,7 @@ def run_pmc_lds(args):
     dev = torch.device("cuda:0")
     w = datagen.WORKLOADS[args.workload]
     rk = Rank(w, 0, dev, torch, np, datagen, vrl)
+    vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
     rk.recv.copy_(rk.packed)
     hm = [torch.empty(w.G, w.S, w.D, dtype=torch.bfloat16, device=dev) for _ in range(3)]
     for _ in range(args.reps):
@@ -854,7 +855,7 @@ def run_pmc_lds(args):
     for _ in range(args.reps):
         vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
     torch.cuda.synchronize()
-    print(f"pmc-lds: {args.reps} x staged unpack (head-major), direct unpack, pack", flush=True)
+    print(f"pmc-sq: {args.reps} x head-run unpack (head-major), direct unpack, pack", flush=True)
 
 
 def sq_summary(d):
@@ -937,8 +938,8 @@ def whole_tensor_grids():
     """{(op, kind, grid in threads): (workload suffix, algorithmic bytes)} for
     the whole-tensor launches of the workloads this benchmark runs.  It
     follows the launch planner's tiling at 16-byte vectors: 256-lane
-    workgroups, 2,048 vectors per direct tile, staged tiles of as many whole
-    token rows as fit 16 KiB."""
+    workgroups, 2,048 vectors per direct tile, head-run tiles of as many
+    tokens of one head as fill 2,048 vectors."""
     import datagen
 
     out = {}
@@ -946,15 +947,15 @@ def whole_tensor_grids():
         w = datagen.WORKLOADS[wid]
         nb = op_bytes(w)
         t_max = -(-w.s_local // w.C)
-        row_vecs = w.G * w.D // 8
-        tt = min(16384 // (w.G * w.D * 2), t_max)
+        head_vecs = w.D // 8
+        row_vecs = w.G * head_vecs
+        tt = min(2048 // head_vecs, t_max)
         for op, nbytes in nb.items():
             blocks = w.P * w.C * (3 if op in ("qkv_pack", "qkv_unpack") else 1)
             direct = 256 * blocks * -(-t_max * row_vecs // 2048)
             out[(op, "direct", direct)] = (suffix, nbytes)
             out[(op, "direct strided-heads", direct)] = (suffix, nbytes)
-            if tt >= 1:
-                out[(op, "staged", 256 * blocks * -(-t_max // tt))] = (suffix, nbytes)
+            out[(op, "head-run", 256 * blocks * w.G * -(-t_max // tt))] = (suffix, nbytes)
     return out
 
 
@@ -1009,8 +1010,8 @@ def main():
         sys.exit(2)
     if args.mode == "pmc":
         run_pmc(args)
-    elif args.mode == "pmc-lds":
-        run_pmc_lds(args)
+    elif args.mode == "pmc-sq":
+        run_pmc_sq(args)
     else:
         run_bench(args)
 

@@ -21,26 +21,15 @@ constexpr int kThreads = VRL_THREADS;
 constexpr int kUnroll = VRL_UNROLL;
 constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
 
-// LDS budget of one workgroup of the staged (transposing) kernel; a tile then
-// holds floor(budget / (G * D * 2)) tokens of all G heads.
-#ifndef VRL_LDS_BYTES
-#define VRL_LDS_BYTES 16384
+// Head-major views (a head's tokens closer together than a token's heads):
+// whether scatters into them (unpack, merge) and gathers from them (pack,
+// split) run as head runs (headrun_kernel) rather than in wire order.
+#ifndef VRL_HEADRUN_SCATTER
+#define VRL_HEADRUN_SCATTER 1
 #endif
-// Scatters into head-major views: 0 = wire order (direct kernel), 1 = view
-// order through LDS, 2 = view order reading the wire buffer directly.
-#ifndef VRL_SCATTER_MODE
-#define VRL_SCATTER_MODE 1
+#ifndef VRL_HEADRUN_GATHER
+#define VRL_HEADRUN_GATHER 0
 #endif
-// Tokens per tile for mode 2.
-#ifndef VRL_VIEW_TOKENS
-#define VRL_VIEW_TOKENS 4
-#endif
-// Whether gathers from head-major views are staged too (scattered reads are
-// cheap, so by default only scatters into head-major views are).
-#ifndef VRL_STAGE_GATHER
-#define VRL_STAGE_GATHER 0
-#endif
-constexpr uint32_t kLdsBytes = VRL_LDS_BYTES;
 
 enum class Op : int { Pack = 0, Unpack = 1, Split = 2, Merge = 3 };
 
@@ -66,18 +55,15 @@ struct KernelArgs {
     uint64_t row_magic;
     uint64_t head_magic;       // j / head_vecs, same scheme
     uint32_t head_shift;
-    uint32_t tile_tokens;      // staged kernel: tokens per tile (TT)
-    uint64_t tv_magic;         // staged kernel: i / (TT * head_vecs)
-    uint32_t tv_shift;
-    uint32_t pad1_;
+    uint32_t tile_tokens;      // head-run kernel: tokens per tile (TT)
+    uint32_t tok_tiles;        // head-run kernel: token tiles per head
 };
 
 struct LaunchPlan {
     Op op;
     int vec_bytes;     // 16, 8, 4 or 2
     bool contig;       // every view row's G heads are one contiguous run
-    bool staged;       // head-major view: view-order traversal (staged_kernel)
-    uint32_t lds_bytes;  // its LDS tile; 0 = read the source directly
+    bool headrun;      // head-major view: runs of one head's tokens (headrun_kernel)
     uint32_t grid;     // workgroups
     KernelArgs args;
 };

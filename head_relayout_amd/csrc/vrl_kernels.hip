@@ -29,8 +29,8 @@
 // and column, obtained with a precomputed multiply-shift division.  Address
 // arithmetic is 64-bit wherever a product can pass 2^31 elements.
 //
-// Views stored head-major, written by a scatter, go through staged_kernel
-// instead: an LDS transpose that writes each head's tokens as one run.
+// Views stored head-major, written by a scatter, go through headrun_kernel
+// instead: each workgroup moves a run of one head's consecutive tokens.
 #include "vrl_internal.h"
 
 namespace vrl {
@@ -137,6 +137,40 @@ struct Block {
     uint16_t *wire;      // first element of the wire block
 };
 
+// Wire block (rank p, chunk c, plane): its token count and the base pointers
+// of the block and of its first view row.
+template <Op OP>
+__device__ __forceinline__ Block block_at(const KernelArgs &a, int64_t p, int32_t c, uint32_t plane)
+{
+    using Tr = Traits<OP>;
+    Block b;
+    b.tile = 0;
+    b.plane = plane;
+    const int64_t nq = Tr::planes3 ? 3 : 1;
+    const int64_t row = int64_t(a.row_heads) * a.D;  // elements per wire row
+    int64_t tok_off, head_off, wire_row0;
+    if (a.chunk_heads) {
+        // chunk c = heads [c*Gc, (c+1)*Gc) of the group, all S_l tokens
+        b.T = a.s_local;
+        tok_off = 0;
+        head_off = int64_t(c) * a.row_heads;
+        wire_row0 = ((p * a.C + c) * nq + plane) * a.s_local;
+    } else {
+        // chunk c = tokens [off(c), off(c) + T(c)), all G heads
+        b.T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
+        tok_off = int64_t(c) * a.chunk_q + (c < a.chunk_r ? c : a.chunk_r);
+        head_off = 0;
+        wire_row0 = p * nq * a.s_local + nq * tok_off + int64_t(plane) * b.T;
+    }
+    const int64_t tok0 = (Tr::hside ? 0 : p * a.s_local) + tok_off;
+    const int64_t head0 = (Tr::hside ? p * a.G : 0) + head_off;
+    b.st = a.view_st[plane];
+    b.sh = a.view_sh[plane];
+    b.view = a.view_ptr[plane] + tok0 * b.st + head0 * b.sh;
+    b.wire = a.wire + wire_row0 * row;
+    return b;
+}
+
 template <Op OP>
 __device__ __forceinline__ Block locate(const KernelArgs &a)
 {
@@ -201,31 +235,8 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
         c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
         p = int64_t(rest / uint32_t(a.n_win));
     }
-    Block b;
+    Block b = block_at<OP>(a, p, c, plane);
     b.tile = tile;
-    b.plane = plane;
-    const int64_t nq = Tr::planes3 ? 3 : 1;
-    const int64_t row = int64_t(a.row_heads) * a.D;  // elements per wire row
-    int64_t tok_off, head_off, wire_row0;
-    if (a.chunk_heads) {
-        // chunk c = heads [c*Gc, (c+1)*Gc) of the group, all S_l tokens
-        b.T = a.s_local;
-        tok_off = 0;
-        head_off = int64_t(c) * a.row_heads;
-        wire_row0 = ((p * a.C + c) * nq + plane) * a.s_local;
-    } else {
-        // chunk c = tokens [off(c), off(c) + T(c)), all G heads
-        b.T = a.chunk_q + (c < a.chunk_r ? 1 : 0);
-        tok_off = int64_t(c) * a.chunk_q + (c < a.chunk_r ? c : a.chunk_r);
-        head_off = 0;
-        wire_row0 = p * nq * a.s_local + nq * tok_off + int64_t(plane) * b.T;
-    }
-    const int64_t tok0 = (Tr::hside ? 0 : p * a.s_local) + tok_off;
-    const int64_t head0 = (Tr::hside ? p * a.G : 0) + head_off;
-    b.st = a.view_st[plane];
-    b.sh = a.view_sh[plane];
-    b.view = a.view_ptr[plane] + tok0 * b.st + head0 * b.sh;
-    b.wire = a.wire + wire_row0 * row;
     return b;
 }
 
@@ -287,110 +298,71 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
     }
 }
 
-// Staged kernel, for views stored head-major (a head's tokens lie closer
-// together than a token's heads): the token and head axes truly swap between
-// the wire rows [token][head][D] and the view's [head][token][D] runs.  A
-// workgroup takes TT tokens of one wire block with all G heads, reads them in
-// the order that is contiguous on the source side into LDS (laid out in wire
-// order), and after a barrier writes them in the order that is contiguous on
-// the destination side: wire rows for a gather, runs of TT tokens per head
-// for a scatter.  Loads are clamped into the tile so that they are never
-// predicated; only LDS writes and global stores test the tile's extent.
-template <Op OP, int VB, bool USE_LDS>
-__global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
+// Head-run kernel, for views stored head-major: a workgroup moves TT
+// consecutive tokens of one head of a wire block (TT * head_vecs <= kTileVecs
+// vectors), and consecutive workgroups take consecutive token tiles of the
+// same head.  The head-major side then sees one contiguous run per
+// workgroup and the chip writes (or reads) few runs at a time; the wire side
+// sees TT pieces of D elements, one per wire row.
+template <Op OP, int VB>
+__global__ __launch_bounds__(kThreads) void headrun_kernel(const KernelArgs a)
 {
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
     constexpr int VE = VB / 2;
-    extern __shared__ __align__(16) unsigned char lds_raw[];
-    V *const lds = reinterpret_cast<V *>(lds_raw);
 
-    const Block b = locate<OP>(a);
-    const uint32_t TT = a.tile_tokens;
-    const uint32_t t0 = b.tile * TT;
+    // workgroup -> (rank, plane, head, chunk, token tile), the token tile
+    // fastest and then the chunk: with token chunks the chunks of a rank are
+    // consecutive token ranges of each head, so one head's runs follow each
+    // other across the whole rank before the next head starts.
+    uint32_t rest = blockIdx.x;
+    const uint32_t tt_i = rest % a.tok_tiles;
+    rest /= a.tok_tiles;
+    const int32_t c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+    rest /= uint32_t(a.n_win);
+    const uint32_t h = rest % uint32_t(a.row_heads);
+    rest /= uint32_t(a.row_heads);
+    uint32_t plane = 0;
+    if (Tr::planes3) {
+        plane = rest % 3u;
+        rest /= 3u;
+    }
+    const Block b = block_at<OP>(a, int64_t(rest), c, plane);
+    const uint32_t t0 = tt_i * a.tile_tokens;
     if (int64_t(t0) >= b.T)
         return;
-    const uint32_t tte = uint32_t(min(int64_t(TT), b.T - t0));  // tokens in this tile
-    const uint32_t nv = TT * a.row_vecs;                           // vectors of a full tile
-    const int64_t st = b.st, sh = b.sh;
-    uint16_t *const view = b.view + int64_t(t0) * st;
-    uint16_t *const wire = b.wire + int64_t(t0) * a.row_heads * a.D;
+    const uint32_t tte = uint32_t(min(int64_t(a.tile_tokens), b.T - t0));
+    const uint32_t nv = tte * a.head_vecs;  // vectors of this tile
+    const int64_t st = b.st, row = int64_t(a.row_heads) * a.D;
+    uint16_t *const view = b.view + int64_t(t0) * st + int64_t(h) * b.sh;
+    uint16_t *const wire = b.wire + int64_t(t0) * row + int64_t(h) * a.D;
 
-    // Wire order: i -> (t, j) with j = h * head_vecs + e; LDS index = i.
-    // View order: i -> (h, t, e); LDS index = t * row_vecs + h * head_vecs + e.
-    struct Pos {
-        uint32_t t, lds;
-        int64_t view_off;
+    // element offset of vector i (token t, column e) on a side whose token stride is `stride`
+    auto off = [&](uint32_t i, int64_t stride) -> int64_t {
+        const uint32_t t = div_magic(i, a.head_magic, a.head_shift);
+        return int64_t(t) * stride + int64_t(i - t * a.head_vecs) * VE;
     };
-    auto wire_order = [&](uint32_t i) -> Pos {
-        const uint32_t t = div_magic(i, a.row_magic, a.row_shift);
-        const uint32_t j = i - t * a.row_vecs;
-        const uint32_t h = div_magic(j, a.head_magic, a.head_shift);
-        const uint32_t e = j - h * a.head_vecs;
-        return Pos{t, i, int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+    auto src_of = [&](uint32_t i) -> const V * {
+        return reinterpret_cast<const V *>(Tr::gather ? view + off(i, st) : wire + off(i, row));
     };
-    auto view_order = [&](uint32_t i) -> Pos {
-        const uint32_t h = div_magic(i, a.tv_magic, a.tv_shift);
-        const uint32_t r = i - h * (TT * a.head_vecs);
-        const uint32_t t = div_magic(r, a.head_magic, a.head_shift);
-        const uint32_t e = r - t * a.head_vecs;
-        return Pos{t, t * a.row_vecs + h * a.head_vecs + e,
-                   int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+    auto dst_of = [&](uint32_t i) -> V * {
+        return reinterpret_cast<V *>(Tr::gather ? wire + off(i, row) : view + off(i, st));
     };
 
-    // Phase 1: source -> LDS, in the source's contiguous order.
-    for (uint32_t i0 = 0; USE_LDS && i0 < nv; i0 += kTileVecs) {
+    if (nv == kTileVecs) {
         V buf[kUnroll];
-        uint32_t slot[kUnroll];
-        bool ok[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
-            const uint32_t ic = i < nv ? i : nv - 1;
-            Pos q = Tr::gather ? view_order(ic) : wire_order(ic);
-            ok[u] = i < nv && q.t < tte;
-            const uint32_t tc = q.t < tte ? q.t : tte - 1;
-            // clamp the token into the tile: the load stays in bounds
-            const V *src = Tr::gather
-                ? reinterpret_cast<const V *>(view + q.view_off - int64_t(q.t - tc) * st)
-                : reinterpret_cast<const V *>(wire + (int64_t(ic) - int64_t(q.t - tc) * a.row_vecs) * VE);
-            buf[u] = load_vec(src);
-            slot[u] = q.lds;
-        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (ok[u])
-                lds[slot[u]] = buf[u];
-    }
-    if (USE_LDS)
-        __syncthreads();
-    // Phase 2: LDS (or, without LDS, the source itself) -> destination, in the destination's contiguous order
-    // (all LDS reads of a batch first, then the stores).
-    for (uint32_t i0 = 0; i0 < nv; i0 += kTileVecs) {
-        V buf[kUnroll];
-        int64_t doff[kUnroll];
-        bool ok[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
-            const uint32_t ic = i < nv ? i : nv - 1;
-            Pos q = Tr::gather ? wire_order(ic) : view_order(ic);
-            ok[u] = i < nv && q.t < tte;
-            doff[u] = Tr::gather ? int64_t(ic) * VE : q.view_off;
-            if (USE_LDS) {
-                buf[u] = lds[q.lds];
-            } else {
-                // read the source directly; the token is clamped into the tile
-                const uint32_t tc = q.t < tte ? q.t : tte - 1;
-                buf[u] = Tr::gather
-                    ? load_vec(reinterpret_cast<const V *>(view + q.view_off - int64_t(q.t - tc) * st))
-                    : load_vec(reinterpret_cast<const V *>(wire + (int64_t(q.lds) - int64_t(q.t - tc) * a.row_vecs) * VE));
-            }
-        }
+            buf[u] = load_vec(src_of(threadIdx.x + uint32_t(u * kThreads)));
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (ok[u])
-                store_vec(reinterpret_cast<V *>((Tr::gather ? wire : view) + doff[u]), buf[u]);
+            store_vec(dst_of(threadIdx.x + uint32_t(u * kThreads)), buf[u]);
+    } else {
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = threadIdx.x + uint32_t(u * kThreads);
+            if (i < nv)
+                store_vec(dst_of(i), load_vec(src_of(i)));
+        }
     }
 }
 
@@ -399,12 +371,9 @@ hipError_t launch_vb(const LaunchPlan &pl, hipStream_t stream)
 {
     KernelArgs args = pl.args;
     void *kargs[] = {&args};
-    if (pl.staged)
-        return pl.lds_bytes
-            ? hipLaunchKernel(reinterpret_cast<const void *>(&staged_kernel<OP, VB, true>), dim3(pl.grid),
-                              dim3(kThreads), kargs, pl.lds_bytes, stream)
-            : hipLaunchKernel(reinterpret_cast<const void *>(&staged_kernel<OP, VB, false>), dim3(pl.grid),
-                              dim3(kThreads), kargs, 0, stream);
+    if (pl.headrun)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&headrun_kernel<OP, VB>), dim3(pl.grid),
+                               dim3(kThreads), kargs, 0, stream);
     const void *fn = pl.contig ? reinterpret_cast<const void *>(&relayout_kernel<OP, VB, true>)
                                : reinterpret_cast<const void *>(&relayout_kernel<OP, VB, false>);
     return hipLaunchKernel(fn, dim3(pl.grid), dim3(kThreads), kargs, 0, stream);

@@ -91,34 +91,34 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     a.tiles = uint32_t((nvec_max + kTileVecs - 1) / kTileVecs);
 
     // A view whose heads lie further apart than its tokens (head-major
-    // storage) makes the token and head axes swap for real.  Writing such a
-    // view row by row scatters 2*D-byte pieces over G heads; those calls go
-    // through the LDS-staged kernel, whose tiles hold TT tokens of all G heads
-    // and write each head's TT tokens as one run.  (Reading such a view
-    // piecewise costs little, so gathers stay direct unless VRL_STAGE_GATHER.)
+    // storage) makes the token and head axes swap for real: in wire order a
+    // workgroup's writes into it scatter 2*D-byte pieces over all Gb heads,
+    // and the chip has every head's stream open at once.  Scatters into such
+    // views run as head runs instead: a workgroup moves TT consecutive
+    // tokens of one head (TT * head_vecs <= kTileVecs), consecutive
+    // workgroups continue the same head.  Gathers from them stay in wire
+    // order, where the scattered side is the reads, which cost little.
     bool head_major = false;
     for (int i = 0; i < nviews; ++i)
         if (views[i].sh > views[i].st)
             head_major = true;
     const bool gather = op == Op::Pack || op == Op::Split;
-    const int64_t row_bytes = Gb * d->D * 2;
-    const bool use_lds = VRL_SCATTER_MODE == 1 && row_bytes <= int64_t(kLdsBytes);
-    if (head_major && (!gather || VRL_STAGE_GATHER) && Gb > 1 &&
-        (use_lds || VRL_SCATTER_MODE == 2)) {
-        const int64_t tt = std::min<int64_t>(
-            {use_lds ? int64_t(kLdsBytes) / row_bytes : int64_t(VRL_VIEW_TOKENS), t_max, 4096});
-        pl.staged = true;
-        pl.lds_bytes = use_lds ? uint32_t(tt * row_bytes) : 0;
+    int64_t tiles = a.tiles;
+    if (head_major && Gb > 1 && (gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER) &&
+        a.head_vecs <= kTileVecs) {
+        const int64_t tt = std::min<int64_t>(kTileVecs / a.head_vecs, t_max);
+        pl.headrun = true;
         a.tile_tokens = uint32_t(tt);
-        magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
-        a.tiles = uint32_t((t_max + tt - 1) / tt);
+        a.tok_tiles = uint32_t((t_max + tt - 1) / tt);
+        tiles = Gb * int64_t(a.tok_tiles);
     }
     const int64_t planes = (op == Op::Pack || op == Op::Unpack) ? 3 : 1;
-    const int64_t grid = int64_t(d->P) * (ce - cb) * planes * a.tiles;
+    const int64_t grid = int64_t(d->P) * (ce - cb) * planes * tiles;
     if (grid >= (int64_t(1) << 31)) {
         *why = "the launch needs 2^31 workgroups or more";
         return false;
     }
+    a.tiles = uint32_t(tiles);
     pl.grid = uint32_t(grid);
     return true;
 }

@@ -59,8 +59,8 @@ def test_pmc_summary_maps_every_kernel_and_calibrates(tmp_path, capsys):
         ("qkv_unpack", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)1, 16, true>(vrl::KernelArgs)",
         ("attn_split", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)2, 16, true>(vrl::KernelArgs)",
         ("head_merge", "direct"): "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)3, 16, true>(vrl::KernelArgs)",
-        ("qkv_unpack", "staged"): "void vrl::(anonymous namespace)::staged_kernel<(vrl::Op)1, 16, true>(vrl::KernelArgs)",
-        ("head_merge", "staged"): "void vrl::(anonymous namespace)::staged_kernel<(vrl::Op)3, 16, true>(vrl::KernelArgs)",
+        ("qkv_unpack", "head-run"): "void vrl::(anonymous namespace)::headrun_kernel<(vrl::Op)1, 16>(vrl::KernelArgs)",
+        ("head_merge", "head-run"): "void vrl::(anonymous namespace)::headrun_kernel<(vrl::Op)3, 16>(vrl::KernelArgs)",
         ("attn_split", "direct strided-heads"):
             "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)2, 16, false>(vrl::KernelArgs)",
     }

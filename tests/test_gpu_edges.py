@@ -196,12 +196,24 @@ def test_split_config5_attention_output(gpu, head_major):
 
 
 @pytest.mark.parametrize("layout", ["dense", "head_major"])
-def test_rows_wider_than_the_lds_tile(gpu, layout):
-    """A head group wider than the staged kernel's 16 KiB LDS tile (66 heads of
-    128: 16,896-byte rows): head-major scatters then run the direct kernel.
-    Random payloads (the shape has more elements than unique 16-bit ids)."""
-    P, C, S_l, H, D = 2, 2, 5, 132, 128
+def test_wide_head_groups(gpu, layout):
+    """66 heads of 128 per group (16,896-byte wire rows), 200 tokens per rank:
+    head-major scatters run as head runs over 66 heads, with ragged chunks
+    and a partial last token tile.  Random payloads (the shape has more
+    elements than unique 16-bit ids)."""
+    P, C, S_l, H, D = 2, 3, 200, 132, 128
     rng = np.random.default_rng(66)
     fused = [rng.integers(0, 0x7F00, size=(S_l, 3 * H * D), dtype=np.uint16) for _ in range(P)]
     lay = {"dense": {}, "head_major": {"head_major": True}}[layout]
-    run_pipeline(gpu, P, C, S_l, H, D, fused, f"wide-rows-{layout}", unpack_layout=lay, merge_layout=lay)
+    run_pipeline(gpu, P, C, S_l, H, D, fused, f"wide-groups-{layout}", unpack_layout=lay, merge_layout=lay)
+
+
+@pytest.mark.parametrize("layout", ["dense", "head_major"])
+def test_head_rows_longer_than_a_tile(gpu, layout):
+    """head_dim 16,392 (2,049 vectors of 16 bytes per head row, more than one
+    workgroup tile): head-major views then fall back to wire order."""
+    P, C, S_l, H, D = 2, 2, 3, 4, 16392
+    rng = np.random.default_rng(16392)
+    fused = [rng.integers(0, 0x7F00, size=(S_l, 3 * H * D), dtype=np.uint16) for _ in range(P)]
+    lay = {"dense": {}, "head_major": {"head_major": True}}[layout]
+    run_pipeline(gpu, P, C, S_l, H, D, fused, f"long-heads-{layout}", unpack_layout=lay, merge_layout=lay)
