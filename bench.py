@@ -559,17 +559,21 @@ def head_chunk_layout(torch, vrl, w, ranks):
 
 def head_major_layouts(torch, vrl, w, rk):
     """Unpack into, and split from, attention-side tensors stored head-major
-    ([G][S][D], viewed as [S][G][D]); checked against the token-major results."""
+    ([G][S][D], viewed as [S][G][D]), and merge into a head-major output
+    ([H][S_l][D], viewed as [S_l][H][D]); checked against the token-major
+    results."""
     P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
     bf = dict(dtype=torch.bfloat16, device=rk.fused.device)
     hm = [torch.empty(G, S, D, **bf) for _ in range(3)]
     views = [t.transpose(0, 1) for t in hm]
     send = torch.empty_like(rk.send)
+    merged = torch.empty(H, S_l, D, **bf)
     nb = op_bytes(w)
     out = {}
     for name, fn, nbytes in (
             ("qkv_unpack", lambda: vrl.qkv_unpack(rk.recv, *views, P, C), nb["qkv_unpack"]),
-            ("attn_split", lambda: vrl.attn_split(views[0], send, P, C), nb["attn_split"])):
+            ("attn_split", lambda: vrl.attn_split(views[0], send, P, C), nb["attn_split"]),
+            ("head_merge", lambda: vrl.head_merge(rk.back, merged.transpose(0, 1), P, C), nb["head_merge"])):
         for _ in range(3):
             fn()
         ts = []
@@ -589,6 +593,8 @@ def head_major_layouts(torch, vrl, w, rk):
             raise SystemExit("head-major unpack differs from token-major unpack")
     if not torch.equal(send.view(torch.int16), rk.send.view(torch.int16)):
         raise SystemExit("split from head-major O differs from split from token-major O")
+    if not torch.equal(merged.transpose(0, 1).contiguous().view(torch.int16), rk.merged.view(torch.int16)):
+        raise SystemExit("merge into a head-major output differs from the token-major merge")
     return out
 
 
