@@ -791,6 +791,8 @@ def kernel_label(name):
           "3": "head_merge"}[name.split("(vrl::Op)")[1][0]]
     if "headrun_kernel" in name:
         return op, "head-run"
+    if "staged_kernel" in name:
+        return op, "staged"
     if name.rstrip().endswith("false>(vrl::KernelArgs)"):
         return op, "direct strided-heads"
     return op, "direct"

@@ -30,6 +30,18 @@ constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
 #ifndef VRL_HEADRUN_GATHER
 #define VRL_HEADRUN_GATHER 0
 #endif
+// Head rows (2*D bytes) narrower than this go through the LDS transpose
+// (staged_kernel) instead of head runs, when a tile of whole wire rows fits
+// the LDS budget.
+#ifndef VRL_HEADRUN_MIN_BYTES
+#define VRL_HEADRUN_MIN_BYTES 128
+#endif
+// LDS budget of one workgroup of the staged kernel; a tile holds
+// floor(budget / (Gb * D * 2)) tokens of all Gb heads of a wire row.
+#ifndef VRL_LDS_BYTES
+#define VRL_LDS_BYTES 16384
+#endif
+constexpr uint32_t kLdsBytes = VRL_LDS_BYTES;
 
 enum class Op : int { Pack = 0, Unpack = 1, Split = 2, Merge = 3 };
 
@@ -55,8 +67,11 @@ struct KernelArgs {
     uint64_t row_magic;
     uint64_t head_magic;       // j / head_vecs, same scheme
     uint32_t head_shift;
-    uint32_t tile_tokens;      // head-run kernel: tokens per tile (TT)
+    uint32_t tile_tokens;      // head-run and staged kernels: tokens per tile (TT)
     uint32_t tok_tiles;        // head-run kernel: token tiles per head
+    uint64_t tv_magic;         // staged kernel: i / (TT * head_vecs)
+    uint32_t tv_shift;
+    uint32_t pad_;
 };
 
 struct LaunchPlan {
@@ -64,6 +79,7 @@ struct LaunchPlan {
     int vec_bytes;     // 16, 8, 4 or 2
     bool contig;       // every view row's G heads are one contiguous run
     bool headrun;      // head-major view: runs of one head's tokens (headrun_kernel)
+    uint32_t lds_bytes;  // nonzero: head-major view through the LDS transpose (staged_kernel)
     uint32_t grid;     // workgroups
     KernelArgs args;
 };

@@ -30,7 +30,9 @@
 // arithmetic is 64-bit wherever a product can pass 2^31 elements.
 //
 // Views stored head-major, written by a scatter, go through headrun_kernel
-// instead: each workgroup moves a run of one head's consecutive tokens.
+// instead (each workgroup moves a run of one head's consecutive tokens), or,
+// when head rows are narrower than a cache line, through staged_kernel (an
+// LDS transpose of a tile of tokens x heads).
 #include "vrl_internal.h"
 
 namespace vrl {
@@ -298,6 +300,104 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
     }
 }
 
+// Staged kernel, for head-major views whose head rows (2*D bytes) are
+// narrower than the cache lines the head runs would read them in: there the
+// token and head axes swap below line granularity, so the swap goes through
+// LDS.  A workgroup takes TT tokens of one wire block with all Gb heads,
+// reads them in the order that is contiguous on the source side into LDS
+// (laid out in wire order), and after a barrier writes them in the order
+// that is contiguous on the destination side: wire rows for a gather, runs
+// of TT tokens per head for a scatter.  Loads are clamped into the tile so that they are never
+// predicated; only LDS writes and global stores test the tile's extent.
+template <Op OP, int VB>
+__global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
+{
+    using Tr = Traits<OP>;
+    using V = typename Vec<VB>::type;
+    constexpr int VE = VB / 2;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    V *const lds = reinterpret_cast<V *>(lds_raw);
+
+    const Block b = locate<OP>(a);
+    const uint32_t TT = a.tile_tokens;
+    const uint32_t t0 = b.tile * TT;
+    if (int64_t(t0) >= b.T)
+        return;
+    const uint32_t tte = uint32_t(min(int64_t(TT), b.T - t0));  // tokens in this tile
+    const uint32_t nv = TT * a.row_vecs;                           // vectors of a full tile
+    const int64_t st = b.st, sh = b.sh;
+    uint16_t *const view = b.view + int64_t(t0) * st;
+    uint16_t *const wire = b.wire + int64_t(t0) * a.row_heads * a.D;
+
+    // Wire order: i -> (t, j) with j = h * head_vecs + e; LDS index = i.
+    // View order: i -> (h, t, e); LDS index = t * row_vecs + h * head_vecs + e.
+    struct Pos {
+        uint32_t t, lds;
+        int64_t view_off;
+    };
+    auto wire_order = [&](uint32_t i) -> Pos {
+        const uint32_t t = div_magic(i, a.row_magic, a.row_shift);
+        const uint32_t j = i - t * a.row_vecs;
+        const uint32_t h = div_magic(j, a.head_magic, a.head_shift);
+        const uint32_t e = j - h * a.head_vecs;
+        return Pos{t, i, int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+    };
+    auto view_order = [&](uint32_t i) -> Pos {
+        const uint32_t h = div_magic(i, a.tv_magic, a.tv_shift);
+        const uint32_t r = i - h * (TT * a.head_vecs);
+        const uint32_t t = div_magic(r, a.head_magic, a.head_shift);
+        const uint32_t e = r - t * a.head_vecs;
+        return Pos{t, t * a.row_vecs + h * a.head_vecs + e,
+                   int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+    };
+
+    // Phase 1: source -> LDS, in the source's contiguous order.
+    for (uint32_t i0 = 0; i0 < nv; i0 += kTileVecs) {
+        V buf[kUnroll];
+        uint32_t slot[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
+            const uint32_t ic = i < nv ? i : nv - 1;
+            Pos q = Tr::gather ? view_order(ic) : wire_order(ic);
+            ok[u] = i < nv && q.t < tte;
+            const uint32_t tc = q.t < tte ? q.t : tte - 1;
+            // clamp the token into the tile: the load stays in bounds
+            const V *src = Tr::gather
+                ? reinterpret_cast<const V *>(view + q.view_off - int64_t(q.t - tc) * st)
+                : reinterpret_cast<const V *>(wire + (int64_t(ic) - int64_t(q.t - tc) * a.row_vecs) * VE);
+            buf[u] = load_vec(src);
+            slot[u] = q.lds;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (ok[u])
+                lds[slot[u]] = buf[u];
+    }
+    __syncthreads();
+    // Phase 2: LDS -> destination, in the destination's contiguous order (all
+    // LDS reads of a batch first, then the stores).
+    for (uint32_t i0 = 0; i0 < nv; i0 += kTileVecs) {
+        V buf[kUnroll];
+        int64_t doff[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
+            const uint32_t ic = i < nv ? i : nv - 1;
+            Pos q = Tr::gather ? wire_order(ic) : view_order(ic);
+            ok[u] = i < nv && q.t < tte;
+            doff[u] = Tr::gather ? int64_t(ic) * VE : q.view_off;
+            buf[u] = lds[q.lds];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (ok[u])
+                store_vec(reinterpret_cast<V *>((Tr::gather ? wire : view) + doff[u]), buf[u]);
+    }
+}
+
 // Head-run kernel, for views stored head-major: a workgroup moves TT
 // consecutive tokens of one head of a wire block (TT * head_vecs <= kTileVecs
 // vectors), and consecutive workgroups take consecutive token tiles of the
@@ -374,6 +474,9 @@ hipError_t launch_vb(const LaunchPlan &pl, hipStream_t stream)
     if (pl.headrun)
         return hipLaunchKernel(reinterpret_cast<const void *>(&headrun_kernel<OP, VB>), dim3(pl.grid),
                                dim3(kThreads), kargs, 0, stream);
+    if (pl.lds_bytes)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&staged_kernel<OP, VB>), dim3(pl.grid),
+                               dim3(kThreads), kargs, pl.lds_bytes, stream);
     const void *fn = pl.contig ? reinterpret_cast<const void *>(&relayout_kernel<OP, VB, true>)
                                : reinterpret_cast<const void *>(&relayout_kernel<OP, VB, false>);
     return hipLaunchKernel(fn, dim3(pl.grid), dim3(kThreads), kargs, 0, stream);

@@ -96,16 +96,28 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     // and the chip has every head's stream open at once.  Scatters into such
     // views run as head runs instead: a workgroup moves TT consecutive
     // tokens of one head (TT * head_vecs <= kTileVecs), consecutive
-    // workgroups continue the same head.  Gathers from them stay in wire
-    // order, where the scattered side is the reads, which cost little.
+    // workgroups continue the same head.  Head rows narrower than a cache
+    // line would make those runs read partial lines on the wire side; such
+    // views go through the LDS transpose, whose tiles read whole wire rows
+    // and write each head's TT tokens as one run.  Gathers from head-major
+    // views stay in wire order, where the scattered side is the reads, which
+    // cost little.
     bool head_major = false;
     for (int i = 0; i < nviews; ++i)
         if (views[i].sh > views[i].st)
             head_major = true;
     const bool gather = op == Op::Pack || op == Op::Split;
+    const int64_t row_bytes = Gb * d->D * 2;
     int64_t tiles = a.tiles;
-    if (head_major && Gb > 1 && (gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER) &&
-        a.head_vecs <= kTileVecs) {
+    if (head_major && Gb > 1 && !(gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER)) {
+        // wire order (direct kernel)
+    } else if (head_major && Gb > 1 && d->D * 2 < VRL_HEADRUN_MIN_BYTES && row_bytes <= int64_t(kLdsBytes)) {
+        const int64_t tt = std::min<int64_t>(int64_t(kLdsBytes) / row_bytes, t_max);
+        pl.lds_bytes = uint32_t(tt * row_bytes);
+        a.tile_tokens = uint32_t(tt);
+        magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
+        tiles = (t_max + tt - 1) / tt;
+    } else if (head_major && Gb > 1 && a.head_vecs <= kTileVecs) {
         const int64_t tt = std::min<int64_t>(kTileVecs / a.head_vecs, t_max);
         pl.headrun = true;
         a.tile_tokens = uint32_t(tt);
