@@ -843,7 +843,9 @@ def run_pmc(args):
 
 def run_pmc_sq(args):
     """The head-run unpack into head-major Q/K/V, the direct unpack into
-    token-major ones and the pack, `reps` launches each, for SQ counter runs."""
+    token-major ones and the pack, then the LDS-transpose unpack into
+    head-major Q/K/V of 16-element heads (221,656 tokens per rank, the same
+    bytes), `reps` launches each, for SQ counter runs."""
     import numpy as np
     import torch
 
@@ -863,7 +865,17 @@ def run_pmc_sq(args):
     for _ in range(args.reps):
         vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
     torch.cuda.synchronize()
-    print(f"pmc-sq: {args.reps} x head-run unpack (head-major), direct unpack, pack", flush=True)
+    del rk, hm
+    n16 = datagen.Workload(0, "16-element heads", P=w.P, C=w.C, s_local=w.s_local * w.D // 16, H=w.H, D=16,
+                           total_tokens=w.P * w.s_local * w.D // 16, seed=w.seed)
+    recv = torch.empty(3 * n16.s_local * n16.H * n16.D, dtype=torch.bfloat16, device=dev)
+    recv.view(torch.int16).random_(-30000, 30000)
+    hm = [torch.empty(n16.G, n16.S, n16.D, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    for _ in range(args.reps):
+        vrl.qkv_unpack(recv, *[t.transpose(0, 1) for t in hm], n16.P, n16.C)
+    torch.cuda.synchronize()
+    print(f"pmc-sq: {args.reps} x head-run unpack (head-major), direct unpack, pack, "
+          f"LDS-transpose unpack (head-major, D=16)", flush=True)
 
 
 def sq_summary(d):

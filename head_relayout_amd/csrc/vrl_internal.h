@@ -36,8 +36,8 @@ constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
 #ifndef VRL_HEADRUN_MIN_BYTES
 #define VRL_HEADRUN_MIN_BYTES 128
 #endif
-// LDS budget of one workgroup of the staged kernel; a tile holds
-// floor(budget / (Gb * D * 2)) tokens of all Gb heads of a wire row.
+// LDS budget of one workgroup of the staged kernel; a tile holds as many
+// tokens of its Gt heads as fit (rows padded by one vector).
 #ifndef VRL_LDS_BYTES
 #define VRL_LDS_BYTES 16384
 #endif
@@ -68,7 +68,10 @@ struct KernelArgs {
     uint64_t head_magic;       // j / head_vecs, same scheme
     uint32_t head_shift;
     uint32_t tile_tokens;      // head-run and staged kernels: tokens per tile (TT)
-    uint32_t tok_tiles;        // head-run kernel: token tiles per head
+    uint32_t tok_tiles;        // head-run and staged kernels: token tiles per block
+    uint32_t group_heads;      // staged kernel: heads per tile (Gt, divides row_heads)
+    uint32_t gv_shift;
+    uint64_t gv_magic;         // staged kernel: i / (Gt * head_vecs)
     uint64_t tv_magic;         // staged kernel: i / (TT * head_vecs)
     uint32_t tv_shift;
     uint32_t pad_;

@@ -301,14 +301,17 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 }
 
 // Staged kernel, for head-major views whose head rows (2*D bytes) are
-// narrower than the cache lines the head runs would read them in: there the
-// token and head axes swap below line granularity, so the swap goes through
-// LDS.  A workgroup takes TT tokens of one wire block with all Gb heads,
-// reads them in the order that is contiguous on the source side into LDS
-// (laid out in wire order), and after a barrier writes them in the order
-// that is contiguous on the destination side: wire rows for a gather, runs
-// of TT tokens per head for a scatter.  Loads are clamped into the tile so that they are never
-// predicated; only LDS writes and global stores test the tile's extent.
+// narrower than a cache line: there the token and head axes swap below line
+// granularity, so the swap goes through LDS.  A workgroup takes TT tokens x
+// Gt heads of one wire block, Gt chosen so that a token's Gt head rows are
+// whole 128-byte lines of the wire row.  It reads the tile in the source's
+// contiguous order into LDS (laid out [token][Gt heads], each LDS row padded
+// by one vector so that the column reads of the other phase spread over the
+// banks), and after a barrier writes it in the destination's contiguous
+// order: runs of TT tokens per head for a scatter, wire-row pieces for a
+// gather.  Workgroups are ordered as the head runs are (rank, plane, head
+// group, chunk, token tile), so one group's runs follow each other across a
+// rank's chunks.
 template <Op OP, int VB>
 __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 {
@@ -318,37 +321,51 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
     extern __shared__ __align__(16) unsigned char lds_raw[];
     V *const lds = reinterpret_cast<V *>(lds_raw);
 
-    const Block b = locate<OP>(a);
+    uint32_t rest = blockIdx.x;
+    const uint32_t tt_i = rest % a.tok_tiles;
+    rest /= a.tok_tiles;
+    const int32_t c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+    rest /= uint32_t(a.n_win);
+    const uint32_t groups = uint32_t(a.row_heads) / a.group_heads;
+    const uint32_t hg = rest % groups;
+    rest /= groups;
+    uint32_t plane = 0;
+    if (Tr::planes3) {
+        plane = rest % 3u;
+        rest /= 3u;
+    }
+    const Block b = block_at<OP>(a, int64_t(rest), c, plane);
     const uint32_t TT = a.tile_tokens;
-    const uint32_t t0 = b.tile * TT;
+    const uint32_t t0 = tt_i * TT;
     if (int64_t(t0) >= b.T)
         return;
     const uint32_t tte = uint32_t(min(int64_t(TT), b.T - t0));  // tokens in this tile
-    const uint32_t nv = TT * a.row_vecs;                           // vectors of a full tile
-    const int64_t st = b.st, sh = b.sh;
-    uint16_t *const view = b.view + int64_t(t0) * st;
-    uint16_t *const wire = b.wire + int64_t(t0) * a.row_heads * a.D;
+    const uint32_t hv = a.head_vecs;
+    const uint32_t gv = a.group_heads * hv;                        // vectors of a tile row
+    const uint32_t lrow = gv + 1;                                  // padded LDS row
+    const uint32_t nv = TT * gv;                                   // vectors of a full tile
+    const int64_t st = b.st, sh = b.sh, row = int64_t(a.row_heads) * a.D;
+    const uint32_t h0 = hg * a.group_heads;
+    uint16_t *const view = b.view + int64_t(t0) * st + int64_t(h0) * sh;
+    uint16_t *const wire = b.wire + int64_t(t0) * row + int64_t(h0) * a.D;
 
-    // Wire order: i -> (t, j) with j = h * head_vecs + e; LDS index = i.
-    // View order: i -> (h, t, e); LDS index = t * row_vecs + h * head_vecs + e.
+    // Tile element i in wire order: token t, column j = h * hv + e.
+    // In view order: head h, token t, column e.
     struct Pos {
         uint32_t t, lds;
-        int64_t view_off;
+        int64_t off;  // element offset on the side being read or written
     };
     auto wire_order = [&](uint32_t i) -> Pos {
-        const uint32_t t = div_magic(i, a.row_magic, a.row_shift);
-        const uint32_t j = i - t * a.row_vecs;
-        const uint32_t h = div_magic(j, a.head_magic, a.head_shift);
-        const uint32_t e = j - h * a.head_vecs;
-        return Pos{t, i, int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+        const uint32_t t = div_magic(i, a.gv_magic, a.gv_shift);
+        const uint32_t j = i - t * gv;
+        return Pos{t, t * lrow + j, int64_t(t) * row + int64_t(j) * VE};
     };
     auto view_order = [&](uint32_t i) -> Pos {
         const uint32_t h = div_magic(i, a.tv_magic, a.tv_shift);
-        const uint32_t r = i - h * (TT * a.head_vecs);
+        const uint32_t r = i - h * (TT * hv);
         const uint32_t t = div_magic(r, a.head_magic, a.head_shift);
-        const uint32_t e = r - t * a.head_vecs;
-        return Pos{t, t * a.row_vecs + h * a.head_vecs + e,
-                   int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+        const uint32_t e = r - t * hv;
+        return Pos{t, t * lrow + h * hv + e, int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
     };
 
     // Phase 1: source -> LDS, in the source's contiguous order.
@@ -359,16 +376,11 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
-            const uint32_t ic = i < nv ? i : nv - 1;
-            Pos q = Tr::gather ? view_order(ic) : wire_order(ic);
+            const Pos q = Tr::gather ? view_order(i < nv ? i : 0) : wire_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
-            const uint32_t tc = q.t < tte ? q.t : tte - 1;
-            // clamp the token into the tile: the load stays in bounds
-            const V *src = Tr::gather
-                ? reinterpret_cast<const V *>(view + q.view_off - int64_t(q.t - tc) * st)
-                : reinterpret_cast<const V *>(wire + (int64_t(ic) - int64_t(q.t - tc) * a.row_vecs) * VE);
-            buf[u] = load_vec(src);
             slot[u] = q.lds;
+            if (ok[u])
+                buf[u] = load_vec(reinterpret_cast<const V *>((Tr::gather ? view : wire) + q.off));
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -385,11 +397,11 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
-            const uint32_t ic = i < nv ? i : nv - 1;
-            Pos q = Tr::gather ? wire_order(ic) : view_order(ic);
+            const Pos q = Tr::gather ? wire_order(i < nv ? i : 0) : view_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
-            doff[u] = Tr::gather ? int64_t(ic) * VE : q.view_off;
-            buf[u] = lds[q.lds];
+            doff[u] = q.off;
+            if (ok[u])
+                buf[u] = lds[q.lds];
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)

@@ -35,6 +35,16 @@ int vector_bytes(const PlanView *vs, int n, uintptr_t wire, int64_t D)
     return 2;
 }
 
+// Heads per tile of the LDS transpose: the smallest divisor of Gb whose head
+// rows fill at least one 128-byte line, else all Gb.
+int64_t staged_heads(int64_t Gb, int64_t D)
+{
+    for (int64_t g = 1; g <= Gb; ++g)
+        if (Gb % g == 0 && g * D * 2 >= 128)
+            return g;
+    return Gb;
+}
+
 }  // namespace
 
 bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, uintptr_t wire,
@@ -107,16 +117,27 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
         if (views[i].sh > views[i].st)
             head_major = true;
     const bool gather = op == Op::Pack || op == Op::Split;
-    const int64_t row_bytes = Gb * d->D * 2;
     int64_t tiles = a.tiles;
     if (head_major && Gb > 1 && !(gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER)) {
         // wire order (direct kernel)
-    } else if (head_major && Gb > 1 && d->D * 2 < VRL_HEADRUN_MIN_BYTES && row_bytes <= int64_t(kLdsBytes)) {
-        const int64_t tt = std::min<int64_t>(int64_t(kLdsBytes) / row_bytes, t_max);
-        pl.lds_bytes = uint32_t(tt * row_bytes);
+    } else if (head_major && Gb > 1 && d->D * 2 < VRL_HEADRUN_MIN_BYTES &&
+               (staged_heads(Gb, d->D) * a.head_vecs + 1) * vb <= int64_t(kLdsBytes)) {
+        // a tile row: Gt heads, whole 128-byte lines of a wire row when Gb allows
+        const int64_t gt = staged_heads(Gb, d->D);
+        const int64_t lrow_bytes = (gt * a.head_vecs + 1) * vb;
+        // tokens per tile: as many as fit, rounded to whole lines of a head's run
+        const int64_t quantum = std::max<int64_t>(1, 128 / (d->D * 2));
+        int64_t tt = int64_t(kLdsBytes) / lrow_bytes;
+        if (tt >= quantum)
+            tt -= tt % quantum;
+        tt = std::min<int64_t>(tt, t_max);
+        a.group_heads = uint32_t(gt);
         a.tile_tokens = uint32_t(tt);
+        a.tok_tiles = uint32_t((t_max + tt - 1) / tt);
+        magic_for(uint32_t(gt * a.head_vecs), a.gv_magic, a.gv_shift);
         magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
-        tiles = (t_max + tt - 1) / tt;
+        pl.lds_bytes = uint32_t(tt * lrow_bytes);
+        tiles = (Gb / gt) * int64_t(a.tok_tiles);
     } else if (head_major && Gb > 1 && a.head_vecs <= kTileVecs) {
         const int64_t tt = std::min<int64_t>(kTileVecs / a.head_vecs, t_max);
         pl.headrun = true;
