@@ -58,6 +58,8 @@ SHAPES = [
     (3, 2, 7, 6, 3, 1),       # odd head_dim, padded rows
     (2, 3, 8, 4, 5, 0),       # odd head_dim, 2-byte vectors throughout
     (2, 2, 4, 4, 256, 0),     # head_dim 256
+    (2, 3, 20, 4, 63, 0),     # 126-byte head rows: LDS transpose when head-major
+    (2, 3, 20, 4, 64, 0),     # 128-byte head rows: head runs when head-major
 ]
 IDS = [f"P{s[0]}C{s[1]}S{s[2]}H{s[3]}D{s[4]}pad{s[5]}" for s in SHAPES]
 
