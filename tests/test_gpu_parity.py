@@ -64,15 +64,20 @@ def test_config4_pad_sentinel_never_copied(gpu):
 
 
 @pytest.mark.gpu
-def test_offsets_beyond_2_31_elements(gpu):
+@pytest.mark.parametrize("layout", ["dense", "head_major"])
+def test_offsets_beyond_2_31_elements(gpu, layout):
     """Wire buffers of 2.2e9 elements (4.4 GB per rank): element offsets pass
     2^31, so every address product must be 64-bit.  P=2, C=2, 90,000
-    tokens/rank, 64 heads of 128; the whole path against the oracle."""
+    tokens/rank, 64 heads of 128; the whole path against the oracle, with
+    token-major or head-major (head-run kernels) attention side and merge
+    output."""
     from dataclasses import replace
     w = replace(WORKLOADS[2], name="large offsets", s_local=90000, H=64, total_tokens=180000, C=2)
     assert 3 * w.s_local * w.H * w.D > 2**31
-    say("[large] generating inputs")
+    say(f"[large-{layout}] generating inputs")
     fused = [datagen.fused_source(w, r) for r in range(w.P)]
-    run_pipeline(gpu, w.P, w.C, w.s_local, w.H, w.D, fused, "large", planes=(1,))
+    lay = {"dense": {}, "head_major": {"head_major": True}}[layout]
+    run_pipeline(gpu, w.P, w.C, w.s_local, w.H, w.D, fused, f"large-{layout}", planes=(1,),
+                 unpack_layout=lay, merge_layout=lay)
     del fused
     torch.cuda.empty_cache()
