@@ -221,20 +221,26 @@ def run_bench(args):
     if not round_trip_ok():
         raise SystemExit("round trip is not bit-exact after timing")
 
-    # A device-to-device copy of the pack's size, for comparison.
-    src = ranks[0].packed
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(10):
+    # Device-to-device copies (hipMemcpyAsync through torch) of the pack's and
+    # of the merge's size, for comparison.
+    copies = {}
+    for name, src in (("qkv", ranks[0].packed), ("attn", ranks[0].send)):
+        dst = torch.empty_like(src)
         dst.copy_(src)
-    b.record()
-    torch.cuda.synchronize()
-    copy_ms = a.elapsed_time(b) / 10
-    copy_gbs = 2 * src.numel() * 2 / (copy_ms * 1e-3) / 1e9
-    del dst
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 10
+        copies[name] = {"bytes": 2 * src.numel() * 2, "ms": round(ms, 5),
+                        "gbs": round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)}
+        del dst
+    for name in per_op:
+        ref = copies["qkv" if name in ("qkv_pack", "qkv_unpack") else "attn"]
+        per_op[name]["pct_of_d2d_copy"] = round(100 * per_op[name]["gbs"] / ref["gbs"], 1)
 
     dominant = "qkv_pack"
     achieved = per_op[dominant]["gbs"]
@@ -263,7 +269,7 @@ def run_bench(args):
                    "bytes_per_step": step_bytes},
         "ops": per_op,
         "roofline": roofline,
-        "copy_d2d": {"bytes": 2 * src.numel() * 2, "ms": round(copy_ms, 5), "gbs": round(copy_gbs, 1)},
+        "copy_d2d": copies,
         "verified": "round trip bit-exact before and after timing",
     }
     say("[bench] the step captured in a HIP graph")
