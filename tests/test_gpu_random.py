@@ -8,6 +8,8 @@ sentinel-filled buffer (with guard bands); the whole buffer, untouched parts
 included, must equal the oracle's result on a buffer filled the same way.
 Values avoid the sentinel and NaN patterns; everything else is random bits.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,9 @@ from tests.gpu_harness import SENTINEL, assert_bits_equal, assert_guard_intact, 
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 600
+# Case count and seed; the environment may ask for a longer or different sweep.
+N_CASES = int(os.environ.get("VRL_RANDOM_CASES", "2000"))
+SEED = int(os.environ.get("VRL_RANDOM_SEED", "20261202"))
 
 
 def _layout(rng, rows, heads, D):
@@ -64,7 +68,7 @@ def _case(rng):
 
 
 def test_random_cases(gpu):
-    rng = np.random.default_rng(20261202)
+    rng = np.random.default_rng(SEED)
     for n in range(N_CASES):
         k = _case(rng)
         P, G, H, D, S_l, C, hc, cb, ce = (k[x] for x in ("P", "G", "H", "D", "S_l", "C", "hc", "cb", "ce"))
