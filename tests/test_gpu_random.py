@@ -1,7 +1,9 @@
 """Seeded random parity sweep of all four relayouts against the oracle.
 
-Each case draws P, the head-group size, head_dim, tokens per rank, the chunk
-reading (tokens or heads) and count, a chunk window, padded source rows, a
+Each case draws P, the head-group size (1-6, 8, 12 or 28 heads: the LDS
+transpose then tiles several heads of a group), head_dim, tokens per rank,
+the chunk reading (tokens or heads) and count, a chunk window, padded source
+rows, a
 source base offset of 0-4 elements, and dense / padded / head-major layouts
 for the attention side and the merge output.  Every op writes into a
 sentinel-filled buffer (with guard bands); the whole buffer, untouched parts
@@ -50,7 +52,7 @@ def _dev_guarded(host, dev):
 
 def _case(rng):
     P = int(rng.choice([1, 2, 3, 4, 8]))
-    G = int(rng.integers(1, 7))
+    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 28]))
     H = P * G
     D = int(rng.choice([2, 4, 6, 8, 16, 24, 64, 128]))
     S_l = int(rng.integers(1, 41))
