@@ -3,9 +3,8 @@
 Each case draws P, the head-group size (1-6, 8, 12 or 28 heads: the LDS
 transpose then tiles several heads of a group), head_dim, tokens per rank,
 the chunk reading (tokens or heads) and count, a chunk window, padded source
-rows, a
-source base offset of 0-4 elements, and dense / padded / head-major layouts
-for the attention side and the merge output.  Every op writes into a
+rows, a source base offset of 0-4 elements, and dense / padded / head-major
+layouts for the attention side and the merge output.  Every op writes into a
 sentinel-filled buffer (with guard bands); the whole buffer, untouched parts
 included, must equal the oracle's result on a buffer filled the same way.
 Values avoid the sentinel and NaN patterns; everything else is random bits.
