@@ -3,8 +3,10 @@
 Ragged chunks, as many chunks as tokens, P = 1, 3, 4 and 8, one head per
 group, small head_dims, padded source rows whose stride forces 2-, 4- and
 8-byte vectors, a source base that is only 2-byte aligned, head-major and
-padded output views, single-chunk windows, two concurrent streams, and the
-representative P=4 attention output read head-major.
+padded output views, single-chunk windows, two concurrent streams, the
+representative P=4 attention output read head-major, head_dims on both sides
+of the 128-byte head-row threshold and beyond one tile, wide head groups, and
+4-D BTHD / BHTD tensors with B = 1 through the binding.
 """
 from __future__ import annotations
 
@@ -219,3 +221,34 @@ def test_head_rows_longer_than_a_tile(gpu, layout):
     fused = [rng.integers(0, 0x7F00, size=(S_l, 3 * H * D), dtype=np.uint16) for _ in range(P)]
     lay = {"dense": {}, "head_major": {"head_major": True}}[layout]
     run_pipeline(gpu, P, C, S_l, H, D, fused, f"long-heads-{layout}", unpack_layout=lay, merge_layout=lay)
+
+
+def test_bthd_tensors_with_batch_one(gpu):
+    """The binding takes BTHD tensors [1][S][G][D] (B = 1) as well as
+    [S][G][D]: unpack into, and split from, 4-D tensors, including a
+    head-major BHTD one viewed as BTHD."""
+    w = WORKLOADS[1]
+    P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+    od = oracle.dims(P, C, S_l, H, D)
+    n = vrl.exchange_elems(vrl.VRL_EXCHANGE_QKV, P, C, S_l, H, D)
+    recv = datagen.values(n, seed=21, stream=0)
+    drecv = to_dev(recv, gpu)
+    bthd = [torch.empty(1, S, G, D, dtype=torch.bfloat16, device=gpu) for _ in range(3)]
+    bhtd = [torch.empty(1, G, S, D, dtype=torch.bfloat16, device=gpu) for _ in range(3)]
+    vrl.qkv_unpack(drecv, *bthd, P, C)
+    vrl.qkv_unpack(drecv, *[t.transpose(1, 2) for t in bhtd], P, C)
+    want = [np.zeros((S, G, D), dtype=np.uint16) for _ in range(3)]
+    oracle.qkv_unpack(od, recv, *want)
+    torch.cuda.synchronize()
+    for q in range(3):
+        assert_bits_equal(bthd[q][0], want[q], f"BTHD unpack plane {q}")
+        assert_bits_equal(bhtd[q][0].transpose(0, 1), want[q], f"BHTD unpack plane {q}")
+    send = torch.empty(vrl.exchange_elems(vrl.VRL_EXCHANGE_ATTN, P, C, S_l, H, D), dtype=torch.bfloat16,
+                       device=gpu)
+    ref = np.zeros(send.numel(), dtype=np.uint16)
+    oracle.attn_split(od, want[2], ref)
+    for o in (bthd[2], bhtd[2].transpose(1, 2)):
+        send.zero_()
+        vrl.attn_split(o, send, P, C)
+        torch.cuda.synchronize()
+        assert_bits_equal(send, ref, "split from a 4-D tensor")
