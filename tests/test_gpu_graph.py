@@ -27,11 +27,23 @@ def _outs(ranks):
     return [t.clone() for rk in ranks for t in (rk.packed, *rk.planes, rk.send, rk.merged)]
 
 
-@pytest.mark.parametrize("chunk_heads", [False, True])
-def test_graph_replays_match_eager(gpu, chunk_heads):
+@pytest.mark.parametrize("chunk_heads,layout", [(False, "token-major"), (True, "token-major"),
+                                                 (False, "head-major"), (False, "head-major, D=16")])
+def test_graph_replays_match_eager(gpu, chunk_heads, layout):
+    """Token-major views run the direct kernel; head-major attention side and
+    merge output the head-run kernel, or with 16-element heads the LDS
+    transpose."""
     w = WORKLOADS[2]
+    if layout == "head-major, D=16":
+        w = datagen.Workload(0, "mid-size, 16-element heads", P=w.P, C=w.C, s_local=w.s_local, H=w.H, D=16,
+                             total_tokens=w.total_tokens, seed=w.seed)
     P, C = w.P, w.C
     ranks = [Rank(to_dev(datagen.fused_source(w, r), gpu), P, C, w.H, w.D) for r in range(P)]
+    if layout != "token-major":
+        for rk in ranks:
+            bf = dict(dtype=torch.bfloat16, device=gpu)
+            rk.planes = [torch.empty(w.G, w.S, w.D, **bf).transpose(0, 1) for _ in range(3)]
+            rk.merged = torch.empty(w.H, w.s_local, w.D, **bf).transpose(0, 1)
     rng = np.random.default_rng(5)
 
     def refill(seed):
