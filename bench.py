@@ -271,6 +271,7 @@ def run_bench(args):
         "roofline": roofline,
         "copy_d2d": copies,
         "verified": "round trip bit-exact before and after timing",
+        "kernel_sources": kernel_source_hash(),
     }
     say("[bench] the step captured in a HIP graph")
     result["graph_replay"] = graph_replay(torch, ops, ranks, step_bytes, args.steps)
