@@ -303,15 +303,15 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 // Staged kernel, for head-major views whose head rows (2*D bytes) are
 // narrower than a cache line: there the token and head axes swap below line
 // granularity, so the swap goes through LDS.  A workgroup takes TT tokens x
-// Gt heads of one wire block, Gt chosen so that a token's Gt head rows are
-// whole 128-byte lines of the wire row.  It reads the tile in the source's
-// contiguous order into LDS (laid out [token][Gt heads], each LDS row padded
-// by one vector so that the column reads of the other phase spread over the
-// banks), and after a barrier writes it in the destination's contiguous
-// order: runs of TT tokens per head for a scatter, wire-row pieces for a
-// gather.  Workgroups are ordered as the head runs are (rank, plane, head
-// group, chunk, token tile), so one group's runs follow each other across a
-// rank's chunks.
+// Gt heads of one wire block, Gt the fewest heads (dividing the group) whose
+// head rows fill at least one 128-byte line of the wire row.  It reads the
+// tile in the source's contiguous order into LDS (laid out [token][Gt
+// heads], each LDS row padded by one vector so that the column reads of the
+// other phase spread over the banks), and after a barrier writes it in the
+// destination's contiguous order: runs of TT tokens per head for a scatter,
+// wire-row pieces for a gather.  Workgroups are ordered as the head runs are
+// (rank, plane, head group, chunk, token tile), so one group's runs follow
+// each other across a rank's chunks.
 template <Op OP, int VB>
 __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 {
