@@ -1,0 +1,119 @@
+// Host-only check of the launch planner's kernel choice and tile geometry
+// (head_relayout_amd/csrc/vrl_plan.cpp), linked without the kernels: for
+// each case it prints the plan and compares it with the rule it should
+// follow.  Prints one line per case and exits 0 when every case holds.
+//
+// The rule: token-major views take the direct kernel; scatters into
+// head-major views take head runs (128 tokens of one head per workgroup at
+// head_dim 128) when a head row fills at least a 128-byte line, the LDS
+// transpose (Gt heads filling a line x as many tokens as fit 16 KiB) below
+// that, and the direct kernel when a head row is longer than one tile or the
+// group has one head; gathers from head-major views stay direct.
+#include "../../head_relayout_amd/csrc/vrl_internal.h"
+
+#include <cstdint>
+#include <cstdio>
+
+using namespace vrl;
+
+namespace {
+
+enum Kind { DIRECT, HEADRUN, STAGED };
+
+const char *name(Kind k)
+{
+    return k == DIRECT ? "direct" : k == HEADRUN ? "head-run" : "staged";
+}
+
+struct Case {
+    const char *what;
+    Op op;
+    int32_t P, C;
+    int64_t S_l;
+    int32_t H, D, chunk_heads;
+    bool head_major;
+    uintptr_t misalign;  // bytes added to the view pointers
+    Kind kind;           // expected kernel
+    int64_t tt;          // expected tokens per tile (0: not checked)
+    int64_t gt;          // expected heads per tile (staged; 0: not checked)
+    int64_t grid;        // expected workgroups (0: not checked)
+    int vb;              // expected vector bytes
+};
+
+bool run(const Case &k)
+{
+    const Problem pb{k.P, k.C, k.S_l, k.H, k.D, k.chunk_heads};
+    const int64_t G = k.H / k.P, S = int64_t(k.P) * k.S_l, HD = int64_t(k.H) * k.D;
+    const bool hside = k.op == Op::Pack || k.op == Op::Merge;
+    const int64_t rows = hside ? k.S_l : S, heads = hside ? k.H : G;
+    PlanView v[3];
+    for (int i = 0; i < 3; ++i) {
+        const uintptr_t base = (uintptr_t(i + 1) << 36) + k.misalign;
+        if (k.head_major)
+            v[i] = PlanView{base, k.D, rows * k.D};
+        else if (k.op == Op::Pack)
+            v[i] = PlanView{(uintptr_t(1) << 36) + 2 * uintptr_t(i) * HD + k.misalign, 3 * HD, k.D};
+        else
+            v[i] = PlanView{base, heads * k.D, k.D};
+    }
+    const int nviews = (k.op == Op::Pack || k.op == Op::Unpack) ? 3 : 1;
+    LaunchPlan pl;
+    const char *why = nullptr;
+    if (!plan_launch(k.op, pb, v, nviews, uintptr_t(1) << 40, 0, k.C, pl, &why)) {
+        std::printf("%-44s planning failed: %s\n", k.what, why);
+        return false;
+    }
+    const Kind got = pl.headrun ? HEADRUN : pl.lds_bytes ? STAGED : DIRECT;
+    bool ok = got == k.kind && pl.vec_bytes == k.vb;
+    if (k.tt && got != DIRECT)
+        ok = ok && pl.args.tile_tokens == uint32_t(k.tt);
+    if (k.gt && got == STAGED)
+        ok = ok && pl.args.group_heads == uint32_t(k.gt);
+    if (k.grid)
+        ok = ok && pl.grid == uint32_t(k.grid);
+    if (got == STAGED)  // the LDS tile fits the budget and holds whole padded rows
+        ok = ok && pl.lds_bytes <= kLdsBytes &&
+             pl.lds_bytes == pl.args.tile_tokens * (pl.args.group_heads * pl.args.head_vecs + 1) * uint32_t(pl.vec_bytes);
+    std::printf("%-44s %-8s vb=%2d tt=%5u gt=%2u grid=%8u lds=%5u %s\n", k.what, name(got), pl.vec_bytes,
+                got == DIRECT ? 0u : pl.args.tile_tokens, got == STAGED ? pl.args.group_heads : 0u, pl.grid,
+                pl.lds_bytes, ok ? "ok" : "UNEXPECTED");
+    return ok;
+}
+
+}  // namespace
+
+int main()
+{
+    // representative shape: P=2, C=4, 27,707 tokens per rank, 56 heads of 128
+    const int64_t R = 27707;
+    const Case cases[] = {
+        {"pack, fused token-major source", Op::Pack, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 36384, 16},
+        {"unpack, token-major", Op::Unpack, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 36384, 16},
+        {"split, token-major", Op::Split, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 12128, 16},
+        {"merge, token-major", Op::Merge, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 12128, 16},
+        // 28 heads x 55 token tiles of 128 per (rank, chunk, plane)
+        {"unpack into head-major, D=128", Op::Unpack, 2, 4, R, 56, 128, 0, true, 0, HEADRUN, 128, 0, 36960, 16},
+        {"merge into head-major, D=128", Op::Merge, 2, 4, R, 56, 128, 0, true, 0, HEADRUN, 128, 0, 12320, 16},
+        {"split from head-major, D=128", Op::Split, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 12128, 16},
+        {"pack from head-major, D=128", Op::Pack, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 36384, 16},
+        {"unpack into head-major, head chunks", Op::Unpack, 2, 4, R, 56, 128, 1, true, 0, HEADRUN, 128, 0, 0, 16},
+        {"unpack into head-major, D=64", Op::Unpack, 2, 4, 2 * R, 56, 64, 0, true, 0, HEADRUN, 256, 0, 0, 16},
+        // 126-byte head rows: 2 heads fill a line; (2*63 + 1) 2-byte vectors per LDS row
+        {"unpack into head-major, D=63", Op::Unpack, 2, 3, 20, 4, 63, 0, true, 0, STAGED, 7, 2, 0, 2},
+        // 4 heads x 32 B fill a line; 9 vectors per LDS row -> 113 tokens, rounded to 112
+        {"unpack into head-major, D=16", Op::Unpack, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
+        {"merge into head-major, D=16", Op::Merge, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
+        {"unpack into head-major, D=32", Op::Unpack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 112, 2, 0, 16},
+        {"unpack into head-major, D=8, 5 heads", Op::Unpack, 2, 4, 64, 10, 8, 0, true, 0, STAGED, 0, 5, 0, 16},
+        {"unpack into head-major, one head per group", Op::Unpack, 2, 4, 64, 2, 128, 0, true, 0, DIRECT, 0, 0, 0, 16},
+        {"unpack into head-major, D=16392", Op::Unpack, 2, 2, 3, 4, 16392, 0, true, 0, DIRECT, 0, 0, 0, 16},
+        {"unpack, views 2-byte aligned", Op::Unpack, 2, 4, 64, 8, 128, 0, false, 2, DIRECT, 0, 0, 0, 2},
+        {"unpack, views 8-byte aligned", Op::Unpack, 2, 4, 64, 8, 128, 0, false, 8, DIRECT, 0, 0, 0, 8},
+    };
+    int bad = 0;
+    for (const Case &k : cases)
+        bad += run(k) ? 0 : 1;
+    std::printf("%s: %d of %zu cases as expected\n", bad ? "FAILED" : "plan rules ok",
+                int(sizeof(cases) / sizeof(cases[0])) - bad, sizeof(cases) / sizeof(cases[0]));
+    return bad ? 1 : 0;
+}
