@@ -42,3 +42,30 @@ def test_allocation_screen_matches_pages():
     for c in range(w.C):
         peak = oracle.attn_split(d, o, recv, c, c + 1)
         assert round(peak / 2**20, 1) == g["split_output_mib"]
+
+
+def test_allocation_screen_head_chunk_reading():
+    """The same screen under the head-chunk reading of the four-chunk layout
+    (chunks split each head group): pack and merge peaks are unchanged, and
+    a one-chunk split window (all tokens, 7 of 28 heads) also rounds to the
+    page's 94.7 MiB, which is why that figure cannot decide the reading."""
+    g = load("allocation_screen.txt")
+    w = WORKLOADS[3]
+    d = oracle.dims(**w.dims())
+    hc = dict(chunk_heads=True)
+
+    fused = np.empty((w.s_local, w.row_stride), dtype=np.uint16)
+    packed = np.empty(oracle.exchange_elems(d, 0), dtype=np.uint16)
+    assert oracle.qkv_pack(d, *qkv_views(fused, w.H, w.D), packed, **hc) == g["pack_reference_peak_bytes"]
+    del fused, packed
+
+    recv = np.empty(oracle.exchange_elems(d, 1), dtype=np.uint16)
+    out = np.empty((w.s_local, w.H, w.D), dtype=np.uint16)
+    assert oracle.head_merge(d, recv, out, **hc) == g["merge_reference_peak_bytes"]
+    del out
+
+    o = np.empty((w.S, w.G, w.D), dtype=np.uint16)
+    for c in range(w.C):
+        peak = oracle.attn_split(d, o, recv, c, c + 1, **hc)
+        assert peak == w.S * (w.G // w.C) * w.D * 2      # 99,301,888 B
+        assert round(peak / 2**20, 1) == g["split_output_mib"]
