@@ -23,7 +23,9 @@ constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
 
 // Head-major views (a head's tokens closer together than a token's heads):
 // whether scatters into them (unpack, merge) and gathers from them (pack,
-// split) run as head runs (headrun_kernel) rather than in wire order.
+// split) run as head runs (headrun_kernel) or, for head rows narrower than
+// VRL_HEADRUN_MIN_BYTES, through the LDS transpose (staged_kernel), rather
+// than in wire order (relayout_kernel).
 #ifndef VRL_HEADRUN_SCATTER
 #define VRL_HEADRUN_SCATTER 1
 #endif
