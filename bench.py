@@ -280,6 +280,7 @@ def run_bench(args):
     if not args.no_extras:
         say("[bench] four-chunk overlap schedule")
         result["overlap"] = overlap_schedule(torch, w, ranks)
+        result["overlap_sdma"] = overlap_schedule(torch, w, ranks, engine="sdma")
         say("[bench] head-chunked layout")
         result["head_chunks"] = head_chunk_layout(torch, vrl, w, ranks)
         say("[bench] head-major (BHTD) attention side")
@@ -474,18 +475,19 @@ def graph_replay(torch, ops, ranks, step_bytes, steps):
             "steps": steps}
 
 
-def overlap_schedule(torch, w, ranks, reps=10):
+def overlap_schedule(torch, w, ranks, reps=10, engine="kernel"):
     """The whole layer, exchanges included: serial (each stage over all
     chunks, one after the other) against the four-chunk overlap schedule
     (per-chunk stages, exchanges on a second stream, event-ordered ready
-    waits).  Exchanges are device copies in one HBM here, so they compete
-    with the kernels for bandwidth; on several GPUs they would use the
+    waits).  Exchanges are device copies in one HBM here -- copy kernels or
+    SDMA copies (engine) -- so they compete with the kernels for bandwidth
+    (and, as kernels, for compute units); on several GPUs they would use the
     links instead."""
     from harness.ulysses import Layer, run_overlapped, run_serial
 
-    layer = Layer(w.P, w.C, w.s_local, w.H, w.D)
+    layer = Layer(w.P, w.C, w.s_local, w.H, w.D, engine)
     comm = torch.cuda.Stream()
-    out = {}
+    out = {"exchange": engine}
     for name, fn in (("serial", lambda: run_serial(layer, ranks)),
                      ("overlapped", lambda: run_overlapped(layer, ranks, comm))):
         for _ in range(2):

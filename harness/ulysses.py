@@ -14,9 +14,36 @@ round trip that must return that plane of the input.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 import head_relayout_amd as vrl
+
+# hipMemcpyKind asking the runtime for a device-to-device copy that uses no
+# compute units (the SDMA engines) instead of a copy kernel.
+_HIP_MEMCPY_D2D_NO_CU = 1024
+_hip = None
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime this process already uses (the one torch loaded, found
+    by its mapped path), so that streams and pointers are that runtime's."""
+    global _hip
+    if _hip is None:
+        name = "libamdhip64.so"
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1]
+                if "/libamdhip64.so" in path:
+                    name = path
+                    break
+        lib = ctypes.CDLL(name)
+        lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        lib.hipMemcpyAsync.restype = ctypes.c_int
+        _hip = lib
+    return _hip
 
 
 class Rank:
@@ -39,9 +66,17 @@ class Rank:
 
 
 class Layer:
-    """Shapes and per-chunk wire offsets of P ranks' Ulysses exchange."""
+    """Shapes and per-chunk wire offsets of P ranks' Ulysses exchange.
 
-    def __init__(self, P: int, C: int, s_local: int, H: int, D: int):
+    engine: how the stand-in exchange copies blocks inside the one HBM --
+    "kernel" (torch copies, run as copy kernels on the compute units) or
+    "sdma" (hipMemcpyAsync on the copy engines, no compute units).  A real
+    run moves the blocks over xGMI with RCCL instead."""
+
+    def __init__(self, P: int, C: int, s_local: int, H: int, D: int, engine: str = "kernel"):
+        if engine not in ("kernel", "sdma"):
+            raise ValueError(f"unknown exchange engine {engine!r}")
+        self.engine = engine
         self.P, self.C, self.s_local, self.H, self.D = P, C, s_local, H, D
         self.G = H // P
         self.off = [vrl.chunk_offset(c, P, C, s_local, H, D) for c in range(C + 1)]
@@ -55,10 +90,19 @@ class Layer:
     def exchange(self, sends, recvs, qkv: bool, chunks=None) -> None:
         """recv_r[block (s, c)] = send_s[block (r, c)] for the given chunks."""
         per_token = (3 if qkv else 1) * self.G * self.D
+        stream = torch.cuda.current_stream().cuda_stream
         for c in (range(self.C) if chunks is None else chunks):
             for s in range(self.P):
                 for r in range(self.P):
-                    recvs[r][self.block(s, c, per_token)].copy_(sends[s][self.block(r, c, per_token)])
+                    dst = recvs[r][self.block(s, c, per_token)]
+                    src = sends[s][self.block(r, c, per_token)]
+                    if self.engine == "kernel":
+                        dst.copy_(src)
+                        continue
+                    rc = _hip_runtime().hipMemcpyAsync(dst.data_ptr(), src.data_ptr(), src.numel() * 2,
+                                                      _HIP_MEMCPY_D2D_NO_CU, stream)
+                    if rc != 0:
+                        raise RuntimeError(f"hipMemcpyAsync failed with HIP error {rc}")
 
 
 def run_serial(layer: Layer, ranks, plane: int = 0) -> None:

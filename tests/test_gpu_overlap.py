@@ -24,11 +24,13 @@ def _buffers(rk):
     return [rk.packed, rk.recv, *rk.planes, rk.send, rk.back, rk.merged]
 
 
+@pytest.mark.parametrize("engine", ["kernel", "sdma"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_overlap_matches_serial(gpu, name):
+def test_overlap_matches_serial(gpu, name, engine):
+    """engine: the stand-in exchange as copy kernels or as SDMA copies."""
     w = CASES[name]
-    say(f"[overlap {name}] inputs")
-    layer = Layer(w.P, w.C, w.s_local, w.H, w.D)
+    say(f"[overlap {name}, {engine} exchange] inputs")
+    layer = Layer(w.P, w.C, w.s_local, w.H, w.D, engine)
     ranks = [Rank(to_dev(datagen.fused_source(w, r), gpu), w.P, w.C, w.H, w.D) for r in range(w.P)]
     plane = 1
     run_serial(layer, ranks, plane)
@@ -47,7 +49,7 @@ def test_overlap_matches_serial(gpu, name):
         for r, rk in enumerate(ranks):
             for i, (g, x) in enumerate(zip(_buffers(rk), want[r])):
                 assert torch.equal(g.view(torch.int16), x.view(torch.int16)), \
-                    f"{name}: run {it}, rank {r}, buffer {i} differs from the serial schedule"
-    say(f"[overlap {name}] ok")
+                    f"{name} ({engine}): run {it}, rank {r}, buffer {i} differs from the serial schedule"
+    say(f"[overlap {name}, {engine} exchange] ok")
     del ranks, want
     torch.cuda.empty_cache()
