@@ -202,3 +202,33 @@ def test_views_reaching_absurdly_far_are_rejected(vrl_lib):
     assert pack(vrl_lib, dims, huge, k, v) == INVALID
     assert "2^48" in _lib.last_error()
     assert pack(vrl_lib, dims, q, k, V(BASE, 96, 1 << 60)) == INVALID
+
+
+def test_error_reasons_are_per_thread(vrl_lib):
+    """Calls from several threads at once: each thread's vrl_last_error names
+    its own failing argument (the reason is thread-local; the library has no
+    shared mutable state on these paths).  ctypes releases the GIL during a
+    call, so the calls really overlap."""
+    import threading
+
+    errors = []
+
+    def worker(t):
+        # H = 4 * P + 1 is never divisible by P: every call fails with a reason naming H and P
+        P = t + 2
+        dims = (P, 1, 8, 4 * P + 1, 8)
+        for _ in range(2000):
+            if pack(vrl_lib, dims, *fused_qkv((2, 1, 8, 4, 8))) != INVALID:
+                errors.append(f"thread {t}: unexpected status")
+                return
+            msg = _lib.last_error()
+            if f"H={4 * P + 1}" not in msg or f"P={P}" not in msg:
+                errors.append(f"thread {t}: reason {msg!r}")
+                return
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
