@@ -5,8 +5,9 @@ group, small head_dims, padded source rows whose stride forces 2-, 4- and
 8-byte vectors, a source base that is only 2-byte aligned, head-major and
 padded output views, single-chunk windows, two concurrent streams, the
 representative P=4 attention output read head-major, head_dims on both sides
-of the 128-byte head-row threshold and beyond one tile, wide head groups, and
-4-D BTHD / BHTD tensors with B = 1 through the binding.
+of the 128-byte head-row threshold and beyond one tile, wide head groups,
+4-D BTHD / BHTD tensors with B = 1 through the binding, and four host
+threads calling at once.
 """
 from __future__ import annotations
 
@@ -252,3 +253,50 @@ def test_bthd_tensors_with_batch_one(gpu):
         vrl.attn_split(o, send, P, C)
         torch.cuda.synchronize()
         assert_bits_equal(send, ref, "split from a 4-D tensor")
+
+
+def test_concurrent_host_threads(gpu):
+    """Four host threads, each with its own stream, pack and merge distinct
+    inputs at the same time (ctypes drops the GIL inside the library): every
+    result equals the oracle's."""
+    import threading
+
+    w = WORKLOADS[1]
+    P, C, S_l, H, D = w.P, w.C, w.s_local, w.H, w.D
+    od = oracle.dims(P, C, S_l, H, D)
+    n_qkv = vrl.exchange_elems(vrl.VRL_EXCHANGE_QKV, P, C, S_l, H, D)
+    n_att = vrl.exchange_elems(vrl.VRL_EXCHANGE_ATTN, P, C, S_l, H, D)
+    hosts = [datagen.values(S_l * 3 * H * D, seed=40 + t, stream=0).reshape(S_l, 3 * H * D) for t in range(4)]
+    backs = [datagen.values(n_att, seed=50 + t, stream=0) for t in range(4)]
+    fused = [to_dev(h, gpu) for h in hosts]
+    dback = [to_dev(b, gpu) for b in backs]
+    packed = [torch.empty(n_qkv, dtype=torch.bfloat16, device=gpu) for _ in range(4)]
+    merged = [torch.empty(S_l, H, D, dtype=torch.bfloat16, device=gpu) for _ in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(gpu)
+            for _ in range(50):
+                vrl.qkv_pack(*dev_qkv(fused[t], H, D), packed[t], P, C, stream=streams[t])
+                vrl.head_merge(dback[t], merged[t], P, C, stream=streams[t])
+            streams[t].synchronize()
+        except Exception as e:          # reported by the main thread
+            errors.append(f"thread {t}: {e}")
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for t in range(4):
+        ref = np.zeros(n_qkv, dtype=np.uint16)
+        oracle.qkv_pack(od, *host_qkv(hosts[t], H, D), ref)
+        assert_bits_equal(packed[t], ref, f"thread {t} pack")
+        m = np.zeros((S_l, H, D), dtype=np.uint16)
+        oracle.head_merge(od, backs[t], m)
+        assert_bits_equal(merged[t], m, f"thread {t} merge")
