@@ -1,0 +1,39 @@
+"""bench.py end to end on the GPU: a short run of the default workload prints
+one JSON line with every field the benchmark contract names, a roofline
+against the 8 TB/s HBM peak, and per-op figures for the four relayouts."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line(gpu):
+    import bench
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--no-cpu-baseline", "--no-extras"], capture_output=True, text=True, cwd=ROOT,
+                       timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    assert d["metric"] == bench.METRIC
+    assert d["unit"] == "GB/s" and d["higher_is_better"] is True and d["scaling"] == "weak"
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["dtype"] == "bf16" and d["data"] == "synthetic" and d["vs_baseline"] is None
+    assert 0 < d["value"] < 8000 and d["ms_per_step"] > 0
+    assert "workload" in d["config"] and d["config"]["bytes_per_step"] == 12710641664
+    roof = d["roofline"]
+    assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
+    assert 0 < roof["frac"] < 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert roof["traffic"] is None or roof["traffic"] > 0
+    assert set(d["ops"]) == {"qkv_pack", "qkv_unpack", "attn_split", "head_merge"}
+    for op in d["ops"].values():
+        assert op["ms"] > 0 and 0 < op["pct_peak"] < 100 and op["launches"] == 6
+    assert d["kernel_sources"] == bench.kernel_source_hash()
