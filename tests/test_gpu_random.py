@@ -49,12 +49,15 @@ def _dev_guarded(host, dev):
     return whole[2048:2048 + host.size].view(host.shape), whole
 
 
-def _case(rng):
-    P = int(rng.choice([1, 2, 3, 4, 8]))
-    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 28]))
-    H = P * G
-    D = int(rng.choice([2, 4, 6, 8, 16, 24, 64, 128]))
-    S_l = int(rng.integers(1, 41))
+def _case(rng, tokens=(1, 41), dims=(2, 4, 6, 8, 16, 24, 64, 128), max_elems=None):
+    while True:
+        P = int(rng.choice([1, 2, 3, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 28]))
+        H = P * G
+        D = int(rng.choice(dims))
+        S_l = int(rng.integers(*tokens))
+        if max_elems is None or 3 * S_l * H * D <= max_elems:
+            break
     hc = bool(rng.integers(0, 2))
     if hc:
         C = int(rng.choice([c for c in range(1, G + 1) if G % c == 0]))
@@ -72,64 +75,81 @@ def test_random_cases(gpu):
     rng = np.random.default_rng(SEED)
     for n in range(N_CASES):
         k = _case(rng)
-        P, G, H, D, S_l, C, hc, cb, ce = (k[x] for x in ("P", "G", "H", "D", "S_l", "C", "hc", "cb", "ce"))
-        S = P * S_l
-        kw = dict(chunk_heads=hc)
-        tag = f"case {n}: {k}"
         if n % 40 == 0:
-            say(f"[random] {tag}")
-        od = oracle.dims(P, C, S_l, H, D)
-        n_qkv = 3 * S_l * H * D
-        n_att = S_l * H * D
-
-        # pack: source rows with padding, device copy shifted by `base` elements
-        fused = rng.integers(0, 0x7F00, size=(S_l, 3 * H * D + k["pad"]), dtype=np.uint16)
-        hq = [fused[:, i * H * D:(i + 1) * H * D].reshape(S_l, H, D) for i in range(3)]
-        flat = to_dev(np.concatenate([np.zeros(k["base"], np.uint16), fused.reshape(-1)]), gpu)
-        dfused = flat[k["base"]:].view(fused.shape)
-        dq = [dfused[:, i * H * D:(i + 1) * H * D].unflatten(1, (H, D)) for i in range(3)]
-        want = _sentinel(n_qkv)
-        oracle.qkv_pack(od, *hq, want, cb, ce, **kw)
-        got, whole = _dev_guarded(_sentinel(n_qkv), gpu)
-        vrl.qkv_pack(*dq, got, P, C, cb, ce, **kw)
-        torch.cuda.synchronize()
-        assert_bits_equal(got, want, f"{tag} pack")
-        assert_guard_intact(whole, f"{tag} pack")
-
-        # unpack into random layouts
-        recv = rng.integers(0, 0x7F00, size=n_qkv, dtype=np.uint16)
-        drecv = to_dev(recv, gpu)
-        lays = [_layout(rng, S, G, D) for _ in range(3)]
-        hbufs = [_sentinel(shape) for shape, _ in lays]
-        oracle.qkv_unpack(od, recv, *[f(b) for b, (_, f) in zip(hbufs, lays)], cb, ce, **kw)
-        dev = [_dev_guarded(_sentinel(shape), gpu) for shape, _ in lays]
-        vrl.qkv_unpack(drecv, *[f(d[0]) for d, (_, f) in zip(dev, lays)], P, C, cb, ce, **kw)
-        torch.cuda.synchronize()
-        for i in range(3):
-            assert_bits_equal(dev[i][0], hbufs[i], f"{tag} unpack plane {i}")
-            assert_guard_intact(dev[i][1], f"{tag} unpack plane {i}")
-
-        # split from a random layout (the first unpacked plane's buffer, fully
-        # overwritten with values first)
-        oshape, of = lays[0]
-        obuf = rng.integers(0, 0x7F00, size=oshape, dtype=np.uint16)
-        dobuf = to_dev(obuf, gpu)
-        want = _sentinel(n_att)
-        oracle.attn_split(od, of(obuf), want, cb, ce, **kw)
-        got, whole = _dev_guarded(_sentinel(n_att), gpu)
-        vrl.attn_split(of(dobuf), got, P, C, cb, ce, **kw)
-        torch.cuda.synchronize()
-        assert_bits_equal(got, want, f"{tag} split")
-        assert_guard_intact(whole, f"{tag} split")
-
-        # merge into a random layout
-        back = rng.integers(0, 0x7F00, size=n_att, dtype=np.uint16)
-        mshape, mf = _layout(rng, S_l, H, D)
-        hm = _sentinel(mshape)
-        oracle.head_merge(od, back, mf(hm), cb, ce, **kw)
-        dm, whole = _dev_guarded(_sentinel(mshape), gpu)
-        vrl.head_merge(to_dev(back, gpu), mf(dm), P, C, cb, ce, **kw)
-        torch.cuda.synchronize()
-        assert_bits_equal(dm, hm, f"{tag} merge")
-        assert_guard_intact(whole, f"{tag} merge")
+            say(f"[random] case {n}: {k}")
+        _run_case(gpu, rng, k, f"case {n}: {k}")
     say(f"[random] {N_CASES} cases ok")
+
+
+def test_random_medium_cases(gpu):
+    """Forty cases of 100-1,500 tokens per rank and head_dims 16-128 (up to
+    six million elements per wire buffer): several token tiles per block and
+    per head, so the full-tile paths, the partial last tiles and the head-run
+    and LDS-transpose tile walks all run, in every layout."""
+    rng = np.random.default_rng(SEED + 1)
+    for n in range(40):
+        k = _case(rng, tokens=(100, 1501), dims=(16, 32, 64, 128), max_elems=6_000_000)
+        say(f"[random medium] case {n}: {k}")
+        _run_case(gpu, rng, k, f"medium case {n}: {k}")
+    say("[random medium] 40 cases ok")
+
+
+def _run_case(gpu, rng, k, tag):
+    """One case: every op into sentinel-filled, guarded buffers, against the oracle."""
+    P, G, H, D, S_l, C, hc, cb, ce = (k[x] for x in ("P", "G", "H", "D", "S_l", "C", "hc", "cb", "ce"))
+    S = P * S_l
+    kw = dict(chunk_heads=hc)
+    od = oracle.dims(P, C, S_l, H, D)
+    n_qkv = 3 * S_l * H * D
+    n_att = S_l * H * D
+
+    # pack: source rows with padding, device copy shifted by `base` elements
+    fused = rng.integers(0, 0x7F00, size=(S_l, 3 * H * D + k["pad"]), dtype=np.uint16)
+    hq = [fused[:, i * H * D:(i + 1) * H * D].reshape(S_l, H, D) for i in range(3)]
+    flat = to_dev(np.concatenate([np.zeros(k["base"], np.uint16), fused.reshape(-1)]), gpu)
+    dfused = flat[k["base"]:].view(fused.shape)
+    dq = [dfused[:, i * H * D:(i + 1) * H * D].unflatten(1, (H, D)) for i in range(3)]
+    want = _sentinel(n_qkv)
+    oracle.qkv_pack(od, *hq, want, cb, ce, **kw)
+    got, whole = _dev_guarded(_sentinel(n_qkv), gpu)
+    vrl.qkv_pack(*dq, got, P, C, cb, ce, **kw)
+    torch.cuda.synchronize()
+    assert_bits_equal(got, want, f"{tag} pack")
+    assert_guard_intact(whole, f"{tag} pack")
+
+    # unpack into random layouts
+    recv = rng.integers(0, 0x7F00, size=n_qkv, dtype=np.uint16)
+    drecv = to_dev(recv, gpu)
+    lays = [_layout(rng, S, G, D) for _ in range(3)]
+    hbufs = [_sentinel(shape) for shape, _ in lays]
+    oracle.qkv_unpack(od, recv, *[f(b) for b, (_, f) in zip(hbufs, lays)], cb, ce, **kw)
+    dev = [_dev_guarded(_sentinel(shape), gpu) for shape, _ in lays]
+    vrl.qkv_unpack(drecv, *[f(d[0]) for d, (_, f) in zip(dev, lays)], P, C, cb, ce, **kw)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert_bits_equal(dev[i][0], hbufs[i], f"{tag} unpack plane {i}")
+        assert_guard_intact(dev[i][1], f"{tag} unpack plane {i}")
+
+    # split from a random layout (the first unpacked plane's buffer, fully
+    # overwritten with values first)
+    oshape, of = lays[0]
+    obuf = rng.integers(0, 0x7F00, size=oshape, dtype=np.uint16)
+    dobuf = to_dev(obuf, gpu)
+    want = _sentinel(n_att)
+    oracle.attn_split(od, of(obuf), want, cb, ce, **kw)
+    got, whole = _dev_guarded(_sentinel(n_att), gpu)
+    vrl.attn_split(of(dobuf), got, P, C, cb, ce, **kw)
+    torch.cuda.synchronize()
+    assert_bits_equal(got, want, f"{tag} split")
+    assert_guard_intact(whole, f"{tag} split")
+
+    # merge into a random layout
+    back = rng.integers(0, 0x7F00, size=n_att, dtype=np.uint16)
+    mshape, mf = _layout(rng, S_l, H, D)
+    hm = _sentinel(mshape)
+    oracle.head_merge(od, back, mf(hm), cb, ce, **kw)
+    dm, whole = _dev_guarded(_sentinel(mshape), gpu)
+    vrl.head_merge(to_dev(back, gpu), mf(dm), P, C, cb, ce, **kw)
+    torch.cuda.synchronize()
+    assert_bits_equal(dm, hm, f"{tag} merge")
+    assert_guard_intact(whole, f"{tag} merge")
