@@ -23,14 +23,18 @@ constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
 
 // Head-major views (a head's tokens closer together than a token's heads):
 // whether scatters into them (unpack, merge) and gathers from them (pack,
-// split) run as head runs (headrun_kernel) or, for head rows narrower than
-// VRL_HEADRUN_MIN_BYTES, through the LDS transpose (staged_kernel), rather
-// than in wire order (relayout_kernel).
+// split) with head rows of at least VRL_HEADRUN_MIN_BYTES run as head runs
+// (headrun_kernel) rather than in wire order (relayout_kernel).
 #ifndef VRL_HEADRUN_SCATTER
 #define VRL_HEADRUN_SCATTER 1
 #endif
 #ifndef VRL_HEADRUN_GATHER
 #define VRL_HEADRUN_GATHER 0
+#endif
+// Whether gathers from head-major views with head rows narrower than
+// VRL_HEADRUN_MIN_BYTES go through the LDS transpose (else wire order).
+#ifndef VRL_STAGE_NARROW_GATHER
+#define VRL_STAGE_NARROW_GATHER 1
 #endif
 // Head rows (2*D bytes) narrower than this go through the LDS transpose
 // (staged_kernel) instead of head runs, when a tile of whole wire rows fits

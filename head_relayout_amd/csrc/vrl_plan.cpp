@@ -107,21 +107,22 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     // views run as head runs instead: a workgroup moves TT consecutive
     // tokens of one head (TT * head_vecs <= kTileVecs), consecutive
     // workgroups continue the same head.  Head rows narrower than a cache
-    // line would make those runs read partial lines on the wire side; such
-    // views go through the LDS transpose, whose tiles read whole wire rows
-    // and write each head's TT tokens as one run.  Gathers from head-major
-    // views stay in wire order, where the scattered side is the reads, which
-    // cost little.
+    // line would make those runs read partial lines on the wire side, and
+    // make wire-order gathers read partial lines of the view; such views go
+    // through the LDS transpose, whose tiles touch whole lines on both
+    // sides.  Gathers from head-major views with wider head rows stay in
+    // wire order, where the scattered side is the reads, which cost little.
     bool head_major = false;
     for (int i = 0; i < nviews; ++i)
         if (views[i].sh > views[i].st)
             head_major = true;
     const bool gather = op == Op::Pack || op == Op::Split;
+    const bool narrow = d->D * 2 < VRL_HEADRUN_MIN_BYTES &&
+                        (staged_heads(Gb, d->D) * a.head_vecs + 1) * vb <= int64_t(kLdsBytes);
     int64_t tiles = a.tiles;
-    if (head_major && Gb > 1 && !(gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER)) {
-        // wire order (direct kernel)
-    } else if (head_major && Gb > 1 && d->D * 2 < VRL_HEADRUN_MIN_BYTES &&
-               (staged_heads(Gb, d->D) * a.head_vecs + 1) * vb <= int64_t(kLdsBytes)) {
+    if (!head_major || Gb <= 1) {
+        // token-major (or one head per row): wire order (direct kernel)
+    } else if (narrow && (gather ? VRL_STAGE_NARROW_GATHER : VRL_HEADRUN_SCATTER)) {
         // a tile row: Gt heads, whole 128-byte lines of a wire row when Gb allows
         const int64_t gt = staged_heads(Gb, d->D);
         const int64_t lrow_bytes = (gt * a.head_vecs + 1) * vb;
@@ -138,7 +139,7 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
         magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
         pl.lds_bytes = uint32_t(tt * lrow_bytes);
         tiles = (Gb / gt) * int64_t(a.tok_tiles);
-    } else if (head_major && Gb > 1 && a.head_vecs <= kTileVecs) {
+    } else if ((gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER) && a.head_vecs <= kTileVecs) {
         const int64_t tt = std::min<int64_t>(kTileVecs / a.head_vecs, t_max);
         pl.headrun = true;
         a.tile_tokens = uint32_t(tt);
