@@ -286,6 +286,9 @@ def run_bench(args):
         say("[bench] head-major (BHTD) attention side")
         result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
         if w.cid == 3:
+            say("[bench] head-major layouts with narrow heads")
+            result["head_major_narrow"] = head_major_narrow(torch, np, datagen, vrl, dev)
+        if w.cid == 3:
             say("[bench] padded source rows (row stride 21,568)")
             result["strided_rows"] = strided_rows(torch, np, datagen, vrl, dev)
             say("[bench] mid-size and P=4 workloads (buffer rotation past the Infinity Cache)")
@@ -604,6 +607,48 @@ def head_major_layouts(torch, vrl, w, rk):
         raise SystemExit("split from head-major O differs from split from token-major O")
     if not torch.equal(merged.transpose(0, 1).contiguous().view(torch.int16), rk.merged.view(torch.int16)):
         raise SystemExit("merge into a head-major output differs from the token-major merge")
+    return out
+
+
+def head_major_narrow(torch, np, datagen, vrl, dev, dims=(16, 32)):
+    """Head-major attention side and merge output with narrow heads (16 and
+    32 elements: head rows below one cache line, the LDS transpose), 56 heads,
+    the token count per rank scaled so every op moves the representative
+    shape's bytes; checked against the token-major results."""
+    base = datagen.WORKLOADS[3]
+    out = {}
+    for D in dims:
+        w = datagen.Workload(0, f"head_dim {D}", P=base.P, C=base.C, s_local=base.s_local * base.D // D,
+                             H=base.H, D=D, total_tokens=base.P * base.s_local * base.D // D, seed=base.seed)
+        P, C, S_l, H, G, S = w.P, w.C, w.s_local, w.H, w.G, w.S
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        rk = Rank(w, 0, dev, torch, np, datagen, vrl)
+        vrl.qkv_pack(*rk.qkv, rk.packed, P, C)
+        vrl.qkv_unpack(rk.packed, *rk.planes, P, C)          # token-major reference results
+        vrl.attn_split(rk.planes[0], rk.send, P, C)
+        vrl.head_merge(rk.send, rk.merged, P, C)
+        hm = [torch.empty(G, S, D, **bf) for _ in range(3)]
+        views = [t.transpose(0, 1) for t in hm]
+        send = torch.empty_like(rk.send)
+        merged = torch.empty(H, S_l, D, **bf)
+        nb = op_bytes(w)
+        res = {"s_local": S_l, "D": D}
+        for name, fn in (("qkv_unpack", lambda: vrl.qkv_unpack(rk.packed, *views, P, C)),
+                         ("attn_split", lambda: vrl.attn_split(views[0], send, P, C)),
+                         ("head_merge", lambda: vrl.head_merge(rk.send, merged.transpose(0, 1), P, C))):
+            ms = _median_ms(torch, fn)
+            gbs = nb[name] / (ms * 1e-3) / 1e9
+            res[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        torch.cuda.synchronize()
+        same = all(torch.equal(views[q].contiguous().view(torch.int16), rk.planes[q].view(torch.int16))
+                   for q in range(3))
+        same = same and torch.equal(send.view(torch.int16), rk.send.view(torch.int16))
+        same = same and torch.equal(merged.transpose(0, 1).contiguous().view(torch.int16),
+                                    rk.merged.view(torch.int16))
+        if not same:
+            raise SystemExit(f"head-major layouts at head_dim {D} differ from the token-major results")
+        out[f"head_dim_{D}"] = res
+        del rk, hm, views, send, merged
     return out
 
 
