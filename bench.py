@@ -1030,6 +1030,21 @@ def whole_tensor_grids():
             out[(op, "direct", direct)] = (suffix, nbytes)
             out[(op, "direct strided-heads", direct)] = (suffix, nbytes)
             out[(op, "head-run", 256 * blocks * w.G * -(-t_max // tt))] = (suffix, nbytes)
+    # the narrow-head workloads (LDS transpose: tiles of Gt heads filling a
+    # 128-byte line x as many tokens as fit 16 KiB, rounded to whole lines)
+    base = datagen.WORKLOADS[3]
+    for D in (16, 32):
+        s_local = base.s_local * base.D // D
+        t_max = -(-s_local // base.C)
+        G, hv = base.G, D // 8
+        gt = next(g for g in range(1, G + 1) if G % g == 0 and g * D * 2 >= 128)
+        quantum = max(1, 128 // (D * 2))
+        tt = 16384 // ((gt * hv + 1) * 16)
+        tt = min(tt - tt % quantum, t_max)
+        for op in ("qkv_unpack", "attn_split", "head_merge"):
+            blocks = base.P * base.C * (3 if op == "qkv_unpack" else 1)
+            nbytes = op_bytes(base)[op]
+            out[(op, "staged", 256 * blocks * (G // gt) * -(-t_max // tt))] = (f" (head_dim {D})", nbytes)
     return out
 
 
