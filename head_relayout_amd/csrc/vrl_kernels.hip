@@ -303,8 +303,10 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 // Staged kernel, for head-major views whose head rows (2*D bytes) are
 // narrower than a cache line: there the token and head axes swap below line
 // granularity, so the swap goes through LDS.  A workgroup takes TT tokens x
-// Gt heads of one wire block, Gt the fewest heads (dividing the group) whose
-// head rows fill at least one 128-byte line of the wire row.  It reads the
+// Gt heads of one wire block: for a scatter Gt is the fewest heads (dividing
+// the group) whose head rows fill at least one 128-byte line of the wire
+// row, for a gather the whole group, so that it writes whole wire rows.  It
+// reads the
 // tile in the source's contiguous order into LDS (laid out [token][Gt
 // heads], each LDS row padded by one vector so that the column reads of the
 // other phase spread over the banks), and after a barrier writes it in the

@@ -110,21 +110,21 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     // line would make those runs read partial lines on the wire side, and
     // make wire-order gathers read partial lines of the view; such views go
     // through the LDS transpose, whose tiles touch whole lines on both
-    // sides.  Gathers from head-major views with wider head rows stay in
+    // sides (for a gather, whole wire rows).  Gathers from head-major views with wider head rows stay in
     // wire order, where the scattered side is the reads, which cost little.
     bool head_major = false;
     for (int i = 0; i < nviews; ++i)
         if (views[i].sh > views[i].st)
             head_major = true;
     const bool gather = op == Op::Pack || op == Op::Split;
-    const bool narrow = d->D * 2 < VRL_HEADRUN_MIN_BYTES &&
-                        (staged_heads(Gb, d->D) * a.head_vecs + 1) * vb <= int64_t(kLdsBytes);
+    // heads per LDS-transpose tile: a gather writes whole wire rows (all Gb
+    // heads, one write stream), a scatter the fewest heads that fill a line
+    const int64_t gt = gather ? Gb : staged_heads(Gb, d->D);
+    const bool narrow = d->D * 2 < VRL_HEADRUN_MIN_BYTES && (gt * a.head_vecs + 1) * vb <= int64_t(kLdsBytes);
     int64_t tiles = a.tiles;
     if (!head_major || Gb <= 1) {
         // token-major (or one head per row): wire order (direct kernel)
     } else if (narrow && (gather ? VRL_STAGE_NARROW_GATHER : VRL_HEADRUN_SCATTER)) {
-        // a tile row: Gt heads, whole 128-byte lines of a wire row when Gb allows
-        const int64_t gt = staged_heads(Gb, d->D);
         const int64_t lrow_bytes = (gt * a.head_vecs + 1) * vb;
         // tokens per tile: as many as fit, rounded to whole lines of a head's run
         const int64_t quantum = std::max<int64_t>(1, 128 / (d->D * 2));

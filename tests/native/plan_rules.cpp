@@ -4,8 +4,9 @@
 // follow.  Prints one line per case and exits 0 when every case holds.
 //
 // The rule: token-major views take the direct kernel; head-major views with
-// head rows narrower than a 128-byte line take the LDS transpose (Gt heads
-// filling a line x as many tokens as fit 16 KiB), scatters or gathers;
+// head rows narrower than a 128-byte line take the LDS transpose (for a
+// scatter Gt heads filling a line, for a gather the whole group, x as many
+// tokens as fit 16 KiB);
 // scatters into head-major views with wider rows take head runs (128 tokens
 // of one head per workgroup at head_dim 128), gathers from them the direct
 // kernel; so does any view whose head row is longer than one tile or whose
@@ -105,8 +106,10 @@ int main()
         {"unpack into head-major, D=16", Op::Unpack, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
         {"merge into head-major, D=16", Op::Merge, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
         {"unpack into head-major, D=32", Op::Unpack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 112, 2, 0, 16},
-        {"split from head-major, D=16", Op::Split, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
-        {"pack from head-major, D=32", Op::Pack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 112, 2, 0, 16},
+        // gathers: whole wire rows (28 heads); 57 vectors per LDS row -> 17 tokens, rounded to 16
+        {"split from head-major, D=16", Op::Split, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 16, 28, 0, 16},
+        // 113 vectors per LDS row -> 9 tokens, rounded to 8
+        {"pack from head-major, D=32", Op::Pack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 8, 28, 0, 16},
         {"unpack into head-major, D=8, 5 heads", Op::Unpack, 2, 4, 64, 10, 8, 0, true, 0, STAGED, 0, 5, 0, 16},
         {"unpack into head-major, one head per group", Op::Unpack, 2, 4, 64, 2, 128, 0, true, 0, DIRECT, 0, 0, 0, 16},
         {"unpack into head-major, D=16392", Op::Unpack, 2, 2, 3, 4, 16392, 0, true, 0, DIRECT, 0, 0, 0, 16},
