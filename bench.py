@@ -1037,14 +1037,17 @@ def whole_tensor_grids():
         s_local = base.s_local * base.D // D
         t_max = -(-s_local // base.C)
         G, hv = base.G, D // 8
-        gt = next(g for g in range(1, G + 1) if G % g == 0 and g * D * 2 >= 128)
         quantum = max(1, 128 // (D * 2))
-        tt = 16384 // ((gt * hv + 1) * 16)
-        tt = min(tt - tt % quantum, t_max)
         for op in ("qkv_unpack", "attn_split", "head_merge"):
+            # a gather's tiles hold the whole group, a scatter's a line's worth of heads
+            gt = G if op == "attn_split" else next(g for g in range(1, G + 1) if G % g == 0 and g * D * 2 >= 128)
+            tt = 16384 // ((gt * hv + 1) * 16)
+            tt = min(tt - tt % quantum, t_max)
             blocks = base.P * base.C * (3 if op == "qkv_unpack" else 1)
             nbytes = op_bytes(base)[op]
-            out[(op, "staged", 256 * blocks * (G // gt) * -(-t_max // tt))] = (f" (head_dim {D})", nbytes)
+            key = (op, "staged", 256 * blocks * (G // gt) * -(-t_max // tt))
+            label = f" (head_dim {D})" if key not in out else out[key][0][:-1] + f", {D})"
+            out[key] = (label, nbytes)
     return out
 
 
