@@ -797,12 +797,25 @@ def cpu_baseline(w, hosts, nbytes, reps=5):
     passes = sorted((one_pass() for _ in range(reps)), key=lambda t: sum(t.values()))
     med = passes[reps // 2]
     total = sum(med.values())
-    return {"value": round(len(hosts) * sum(nbytes.values()) / total / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"one step of the workload (the pack, unpack, split and merge chains for each "
-                      f"of the {len(hosts)} ranks, each rank's packed buffer standing in for its "
-                      f"exchanged one); median of {reps} timed passes after one untimed pass",
-            "ms": {k: round(1e3 * v, 1) for k, v in med.items()}}
+    cores = oracle.threads()
+    result = {"value": round(len(hosts) * sum(nbytes.values()) / total / 1e9, 3), "unit": "GB/s",
+              "cores": cores, "kind": "oracle",
+              "sample": f"one step of the workload (the pack, unpack, split and merge chains for each "
+                        f"of the {len(hosts)} ranks, each rank's packed buffer standing in for its "
+                        f"exchanged one); median of {reps} timed passes after one untimed pass",
+              "ms": {k: round(1e3 * v, 1) for k, v in med.items()}}
+    # the same chains on one thread, one rank, one pass
+    say("[bench] cpu baseline: one thread, one rank")
+    del bufs[1:]
+    oracle.set_threads(1)
+    try:
+        t1 = one_pass()
+    finally:
+        oracle.set_threads(cores)
+    result["single_thread"] = {"value": round(sum(nbytes.values()) / sum(t1.values()) / 1e9, 3), "unit": "GB/s",
+                               "sample": "rank 0's four chains, one pass",
+                               "ms": {k: round(1e3 * v, 1) for k, v in t1.items()}}
+    return result
 
 
 def read_traffic():
