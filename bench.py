@@ -755,6 +755,11 @@ def smaller_workloads(torch, np, datagen, vrl, dev, wids=(2, 5), reps=12):
     return out
 
 
+def _sig(x, digits=4):
+    """x rounded to `digits` significant digits (a small rate stays nonzero)."""
+    return float(f"{x:.{digits}g}")
+
+
 def cpu_baseline(w, hosts, nbytes, reps=5):
     """The oracle's four chains for every rank (one step of the workload) on
     the host cores: one untimed pass, then `reps` timed passes; the median
@@ -798,7 +803,7 @@ def cpu_baseline(w, hosts, nbytes, reps=5):
     med = passes[reps // 2]
     total = sum(med.values())
     cores = oracle.threads()
-    result = {"value": round(len(hosts) * sum(nbytes.values()) / total / 1e9, 3), "unit": "GB/s",
+    result = {"value": _sig(len(hosts) * sum(nbytes.values()) / total / 1e9), "unit": "GB/s",
               "cores": cores, "kind": "oracle",
               "sample": f"one step of the workload (the pack, unpack, split and merge chains for each "
                         f"of the {len(hosts)} ranks, each rank's packed buffer standing in for its "
@@ -812,7 +817,7 @@ def cpu_baseline(w, hosts, nbytes, reps=5):
         t1 = one_pass()
     finally:
         oracle.set_threads(cores)
-    result["single_thread"] = {"value": round(sum(nbytes.values()) / sum(t1.values()) / 1e9, 3), "unit": "GB/s",
+    result["single_thread"] = {"value": _sig(sum(nbytes.values()) / sum(t1.values()) / 1e9), "unit": "GB/s",
                                "sample": "rank 0's four chains, one pass",
                                "ms": {k: round(1e3 * v, 1) for k, v in t1.items()}}
     return result

@@ -147,10 +147,14 @@ bool disjoint(const Geom &a, const Geom &b)
     outer_inner(a, n, s, w);
     if (n < 2 || s <= 0)
         return false;
-    const int64_t delta = (int64_t(b.ptr) - int64_t(a.ptr)) / 2;
-    if ((int64_t(b.ptr) - int64_t(a.ptr)) % 2 != 0)
+    // m = (b - a) / 2 mod s, the offset of b's slices within a's period,
+    // from the exact unsigned distance between the pointers.
+    const bool ahead = b.ptr >= a.ptr;
+    const uintptr_t dist = ahead ? b.ptr - a.ptr : a.ptr - b.ptr;
+    if (dist % 2 != 0)
         return false;
-    const int64_t m = ((delta % s) + s) % s;
+    const int64_t rem = int64_t((dist / 2) % uintptr_t(s));
+    const int64_t m = ahead || rem == 0 ? rem : s - rem;
     return m >= w && s - m >= w;
 }
 
@@ -170,6 +174,10 @@ vrl_status check_layout(const Geom *gs, int n)
             (g.heads > 1 && g.sh > kMaxReach / (g.heads - 1)) ||
             (g.rows - 1) * g.st + (g.heads - 1) * g.sh + g.D > kMaxReach)
             return fail(VRL_E_INVALID, "%s reaches beyond 2^48 elements", g.name);
+        uintptr_t lo, hi;
+        span(g, lo, hi);
+        if (hi < lo)
+            return fail(VRL_E_INVALID, "%s extends past the end of the address space", g.name);
         if (g.ptr % 2 != 0)
             return fail(VRL_E_LAYOUT, "%s is not 2-byte aligned", g.name);
         if (g.output && !self_disjoint(g))

@@ -45,7 +45,8 @@ def test_oracle_under_asan(tmp_path):
                 _path(P, C, S_l, H, D, unique_fused(P, S_l, H, D, pad), True)
         print("asan ok")
     """)
-    env = dict(os.environ, LD_PRELOAD=_libasan(), ASAN_OPTIONS="detect_leaks=0",
+    preload = " ".join(x for x in (_libasan(), os.environ.get("LD_PRELOAD", "")) if x)
+    env = dict(os.environ, LD_PRELOAD=preload, ASAN_OPTIONS="detect_leaks=0",
                OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, env=env,
                        timeout=300)
