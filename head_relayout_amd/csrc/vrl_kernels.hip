@@ -306,14 +306,13 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 // Gt heads of one wire block: for a scatter Gt is the fewest heads (dividing
 // the group) whose head rows fill at least one 128-byte line of the wire
 // row, for a gather the whole group, so that it writes whole wire rows.  It
-// reads the
-// tile in the source's contiguous order into LDS (laid out [token][Gt
-// heads], each LDS row padded by one vector so that the column reads of the
-// other phase spread over the banks), and after a barrier writes it in the
-// destination's contiguous order: runs of TT tokens per head for a scatter,
-// wire-row pieces for a gather.  Workgroups are ordered as the head runs are
-// (rank, plane, head group, chunk, token tile), so one group's runs follow
-// each other across a rank's chunks.
+// reads the tile in the source's contiguous order into LDS (laid out
+// [token][Gt heads], each LDS row padded by one vector so that the column
+// reads of the other phase spread over the banks), and after a barrier
+// writes it in the destination's contiguous order: runs of TT tokens per
+// head for a scatter, wire-row pieces for a gather.  Workgroups are ordered
+// as the head runs are (rank, plane, head group, chunk, token tile), so one
+// group's runs follow each other across a rank's chunks.
 template <Op OP, int VB>
 __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 {

@@ -110,8 +110,9 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     // line would make those runs read partial lines on the wire side, and
     // make wire-order gathers read partial lines of the view; such views go
     // through the LDS transpose, whose tiles touch whole lines on both
-    // sides (for a gather, whole wire rows).  Gathers from head-major views with wider head rows stay in
-    // wire order, where the scattered side is the reads, which cost little.
+    // sides (for a gather, whole wire rows).  Gathers from head-major views
+    // with wider head rows stay in wire order, where the scattered side is
+    // the reads, which cost little.
     bool head_major = false;
     for (int i = 0; i < nviews; ++i)
         if (views[i].sh > views[i].st)
