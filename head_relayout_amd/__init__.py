@@ -74,7 +74,7 @@ def exchange_elems(which: int, P: int, C: int, s_local: int, H: int, D: int,
     """Elements of one rank's wire buffer (which: VRL_EXCHANGE_QKV or _ATTN)."""
     n = _lib.lib().vrl_exchange_elems(which, ctypes.byref(_dims(P, C, s_local, H, D, chunk_heads)))
     if n < 0:
-        raise ValueError("invalid dimensions")
+        raise ValueError(f"invalid dimensions: {_lib.last_error()}")
     return n
 
 
@@ -84,7 +84,7 @@ def chunk_offset(c: int, P: int, C: int, s_local: int, H: int, D: int,
     gives s_local), or with chunk_heads its first head within a head group."""
     n = _lib.lib().vrl_chunk_offset(ctypes.byref(_dims(P, C, s_local, H, D, chunk_heads)), int(c))
     if n < 0:
-        raise ValueError("invalid arguments")
+        raise ValueError(f"invalid arguments: {_lib.last_error()}")
     return n
 
 

@@ -289,15 +289,25 @@ extern "C" {
 
 VRL_EXPORT int64_t vrl_exchange_elems(int which, const vrl_dims *dims)
 {
-    if (check_dims(dims) != VRL_OK || (which != VRL_EXCHANGE_QKV && which != VRL_EXCHANGE_ATTN))
+    g_error[0] = 0;
+    if (check_dims(dims) != VRL_OK)
         return -1;
+    if (which != VRL_EXCHANGE_QKV && which != VRL_EXCHANGE_ATTN) {
+        fail(VRL_E_INVALID, "which must be VRL_EXCHANGE_QKV or VRL_EXCHANGE_ATTN, got %d", which);
+        return -1;
+    }
     return (which == VRL_EXCHANGE_QKV ? 3 : 1) * dims->s_local * dims->H * dims->D;
 }
 
 VRL_EXPORT int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c)
 {
-    if (check_dims(dims) != VRL_OK || c < 0 || c > dims->C)
+    g_error[0] = 0;
+    if (check_dims(dims) != VRL_OK)
         return -1;
+    if (c < 0 || c > dims->C) {
+        fail(VRL_E_INVALID, "chunk index %d outside [0, C=%d]", c, dims->C);
+        return -1;
+    }
     if (dims->chunk_heads)
         return int64_t(c) * (dims->H / dims->P / dims->C);
     const int64_t q = dims->s_local / dims->C, r = dims->s_local % dims->C;

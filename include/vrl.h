@@ -113,12 +113,15 @@ typedef struct {
 enum { VRL_EXCHANGE_QKV = 0, VRL_EXCHANGE_ATTN = 1 };
 
 /* Elements of one rank's wire buffer: 3*S_l*H*D for VRL_EXCHANGE_QKV,
- * S_l*H*D for VRL_EXCHANGE_ATTN.  Returns -1 for invalid arguments. */
+ * S_l*H*D for VRL_EXCHANGE_ATTN.  Returns -1 for invalid arguments (the
+ * dimension rules of VRL_E_INVALID below, or another `which`), with the
+ * reason in vrl_last_error(). */
 int64_t vrl_exchange_elems(int which, const vrl_dims *dims);
 
 /* Start of chunk c along the chunked axis, for c in [0, C]: the first local
  * token off(c) (off(C) = S_l), or with chunk_heads the first head of the
- * chunk within a head group, c*Gc.  Returns -1 for invalid arguments. */
+ * chunk within a head group, c*Gc.  Returns -1 for invalid dimensions or c
+ * outside [0, C], with the reason in vrl_last_error(). */
 int64_t vrl_chunk_offset(const vrl_dims *dims, int32_t c);
 
 /*
@@ -172,9 +175,10 @@ vrl_status vrl_head_merge(const vrl_dims *dims, const void *recv, const vrl_view
 /* Static name of a status ("VRL_OK", ...). */
 const char *vrl_status_string(vrl_status status);
 
-/* Human-readable reason for the last non-OK status returned on the calling
- * thread (empty if none).  The string is owned by the library and valid
- * until the thread's next vrl call. */
+/* Human-readable reason for the last non-OK status (or -1 from the two
+ * sizing helpers) returned on the calling thread; empty after a call that
+ * succeeded.  The string is owned by the library and valid until the
+ * thread's next vrl call. */
 const char *vrl_last_error(void);
 
 #ifdef __cplusplus

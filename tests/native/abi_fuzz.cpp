@@ -269,9 +269,12 @@ int main()
             if (s != VRL_OK)
                 report(it, "in-contract call rejected", op, s);
         }
-        (void)vrl_exchange_elems(int(below(3)) - 1, &d);
+        // the sizing helpers: -1 exactly when a reason is recorded
+        if ((vrl_exchange_elems(int(below(3)) - 1, &d) < 0) != (vrl_last_error()[0] != 0))
+            report(it, "exchange_elems result and reason disagree", -1, VRL_OK);
         for (int32_t c = -1; c <= 5; ++c)
-            (void)vrl_chunk_offset(&d, c);
+            if ((vrl_chunk_offset(&d, c) < 0) != (vrl_last_error()[0] != 0))
+                report(it, "chunk_offset result and reason disagree", -1, VRL_OK);
         (void)vrl_status_string(vrl_status(int(below(6)) - 1));
     }
     if (g_launch_bad) {

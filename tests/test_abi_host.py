@@ -19,6 +19,7 @@ import subprocess
 import pytest
 import torch
 
+import head_relayout_amd as vrl
 from head_relayout_amd import _lib
 from tests import index_maps as im
 
@@ -70,8 +71,21 @@ def test_host_helpers(vrl_lib, P, C, S, H, D):
         if c < C:
             assert got == im.off(S, C, c)
     assert vrl_lib.vrl_chunk_offset(_d(P, C, S, H, D), C + 1) == -1
+    assert "outside" in _lib.last_error()
     assert vrl_lib.vrl_chunk_offset(_d(P, C, S, H, D), -1) == -1
     assert vrl_lib.vrl_exchange_elems(2, _d(P, C, S, H, D)) == -1
+    assert "VRL_EXCHANGE_QKV" in _lib.last_error()
+    assert vrl_lib.vrl_exchange_elems(0, _d(P, C, S, H, D)) > 0
+    assert _lib.last_error() == ""
+
+
+def test_sizing_errors_carry_the_reason():
+    with pytest.raises(ValueError, match="not divisible"):
+        vrl.exchange_elems(vrl.VRL_EXCHANGE_QKV, 3, 1, 8, 4, 8)
+    with pytest.raises(ValueError, match="exceeds s_local"):
+        vrl.chunk_offset(0, 2, 9, 8, 4, 8)
+    with pytest.raises(ValueError, match="outside"):
+        vrl.chunk_offset(5, 2, 4, 8, 4, 8)
 
 
 BASE = 0x7F0000000000  # fake, 4 KiB aligned; never dereferenced
