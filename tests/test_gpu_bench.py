@@ -36,4 +36,7 @@ def test_bench_json_line(gpu):
     assert set(d["ops"]) == {"qkv_pack", "qkv_unpack", "attn_split", "head_merge"}
     for op in d["ops"].values():
         assert op["ms"] > 0 and 0 < op["pct_peak"] < 100 and op["launches"] == 6
+        assert op["pct_of_d2d_copy"] > 0 and op["pct_of_elementwise_copy"] > 0
+    for key in ("qkv", "attn"):
+        assert d["copy_elementwise"][key]["gbs"] > 0 and d["copy_d2d"][key]["gbs"] > 0
     assert d["kernel_sources"] == bench.kernel_source_hash()
