@@ -300,6 +300,51 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
     }
 }
 
+// Workgroup -> (rank p, chunk c, head or head group g, plane) for the
+// head-run and staged kernels, after the token tile has been taken off
+// `rest`: the workgroups that continue one head-major run come next to each
+// other.  For the unpack, which writes the [S][G][D] side, a head's run is
+// the whole sequence, rank after rank, so the rank varies right after the
+// token tile (with token chunks after the chunk, whose tokens come first
+// within a rank): fewer head runs are written at once.  Otherwise the chunk
+// follows the token tile and the rank varies slowest: on the [S_l][H][D]
+// side each rank has heads of its own, and a gather (split) keeps writing
+// one rank's wire block at a time.
+template <Op OP>
+__device__ __forceinline__ void decode_run(const KernelArgs &a, uint32_t rest, uint32_t groups, int64_t &p,
+                                           int32_t &c, uint32_t &g, uint32_t &plane)
+{
+    using Tr = Traits<OP>;
+    plane = 0;
+    if (!Tr::hside && !Tr::gather) {
+        if (a.chunk_heads) {
+            p = int64_t(rest % uint32_t(a.P));
+            rest /= uint32_t(a.P);
+            c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+            rest /= uint32_t(a.n_win);
+        } else {
+            c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+            rest /= uint32_t(a.n_win);
+            p = int64_t(rest % uint32_t(a.P));
+            rest /= uint32_t(a.P);
+        }
+        g = rest % groups;
+        rest /= groups;
+        if (Tr::planes3)
+            plane = rest;
+        return;
+    }
+    c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+    rest /= uint32_t(a.n_win);
+    g = rest % groups;
+    rest /= groups;
+    if (Tr::planes3) {
+        plane = rest % 3u;
+        rest /= 3u;
+    }
+    p = int64_t(rest);
+}
+
 // Staged kernel, for head-major views whose head rows (2*D bytes) are
 // narrower than a cache line: there the token and head axes swap below line
 // granularity, so the swap goes through LDS.  A workgroup takes TT tokens x
@@ -311,8 +356,7 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 // reads of the other phase spread over the banks), and after a barrier
 // writes it in the destination's contiguous order: runs of TT tokens per
 // head for a scatter, wire-row pieces for a gather.  Workgroups are ordered
-// as the head runs are (rank, plane, head group, chunk, token tile), so one
-// group's runs follow each other across a rank's chunks.
+// as the head runs are (decode_run), token tile fastest.
 template <Op OP, int VB>
 __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 {
@@ -322,20 +366,13 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
     extern __shared__ __align__(16) unsigned char lds_raw[];
     V *const lds = reinterpret_cast<V *>(lds_raw);
 
-    uint32_t rest = blockIdx.x;
-    const uint32_t tt_i = rest % a.tok_tiles;
-    rest /= a.tok_tiles;
-    const int32_t c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
-    rest /= uint32_t(a.n_win);
+    const uint32_t tt_i = blockIdx.x % a.tok_tiles;
     const uint32_t groups = uint32_t(a.row_heads) / a.group_heads;
-    const uint32_t hg = rest % groups;
-    rest /= groups;
-    uint32_t plane = 0;
-    if (Tr::planes3) {
-        plane = rest % 3u;
-        rest /= 3u;
-    }
-    const Block b = block_at<OP>(a, int64_t(rest), c, plane);
+    int64_t p;
+    int32_t c;
+    uint32_t hg, plane;
+    decode_run<OP>(a, blockIdx.x / a.tok_tiles, groups, p, c, hg, plane);
+    const Block b = block_at<OP>(a, p, c, plane);
     const uint32_t TT = a.tile_tokens;
     const uint32_t t0 = tt_i * TT;
     if (int64_t(t0) >= b.T)
@@ -424,23 +461,13 @@ __global__ __launch_bounds__(kThreads) void headrun_kernel(const KernelArgs a)
     using V = typename Vec<VB>::type;
     constexpr int VE = VB / 2;
 
-    // workgroup -> (rank, plane, head, chunk, token tile), the token tile
-    // fastest and then the chunk: with token chunks the chunks of a rank are
-    // consecutive token ranges of each head, so one head's runs follow each
-    // other across the whole rank before the next head starts.
-    uint32_t rest = blockIdx.x;
-    const uint32_t tt_i = rest % a.tok_tiles;
-    rest /= a.tok_tiles;
-    const int32_t c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
-    rest /= uint32_t(a.n_win);
-    const uint32_t h = rest % uint32_t(a.row_heads);
-    rest /= uint32_t(a.row_heads);
-    uint32_t plane = 0;
-    if (Tr::planes3) {
-        plane = rest % 3u;
-        rest /= 3u;
-    }
-    const Block b = block_at<OP>(a, int64_t(rest), c, plane);
+    // token tile fastest, then what continues the same head's run
+    const uint32_t tt_i = blockIdx.x % a.tok_tiles;
+    int64_t p;
+    int32_t c;
+    uint32_t h, plane;
+    decode_run<OP>(a, blockIdx.x / a.tok_tiles, uint32_t(a.row_heads), p, c, h, plane);
+    const Block b = block_at<OP>(a, p, c, plane);
     const uint32_t t0 = tt_i * a.tile_tokens;
     if (int64_t(t0) >= b.T)
         return;
