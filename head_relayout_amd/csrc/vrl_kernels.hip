@@ -226,16 +226,27 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
         c = a.c_begin + int32_t(rest);
     } else {
         // Unpack and split: one rank's blocks are one contiguous token range
-        // of the [S][G][D] side; blocks run in wire-buffer order.
+        // of the [S][G][D] side.  The unpack with token chunks takes the
+        // planes one after the other, and within a plane the blocks in token
+        // order (chunk fastest, then rank), so consecutive blocks write
+        // adjacent rows of one output tensor; otherwise blocks run in
+        // wire-buffer order.
         const uint32_t blk = wg / a.tiles;
         tile = wg - blk * a.tiles;
         rest = blk;
-        if (Tr::planes3) {
-            plane = rest % 3u;
-            rest /= 3u;
+        if (Tr::planes3 && !a.chunk_heads) {
+            c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+            rest /= uint32_t(a.n_win);
+            p = int64_t(rest % uint32_t(a.P));
+            plane = rest / uint32_t(a.P);
+        } else {
+            if (Tr::planes3) {
+                plane = rest % 3u;
+                rest /= 3u;
+            }
+            c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
+            p = int64_t(rest / uint32_t(a.n_win));
         }
-        c = a.c_begin + int32_t(rest % uint32_t(a.n_win));
-        p = int64_t(rest / uint32_t(a.n_win));
     }
     Block b = block_at<OP>(a, p, c, plane);
     b.tile = tile;
