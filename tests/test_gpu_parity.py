@@ -81,3 +81,39 @@ def test_offsets_beyond_2_31_elements(gpu, layout):
                  unpack_layout=lay, merge_layout=lay)
     del fused
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("layout", ["dense", "head_major"])
+def test_unpack_eight_ranks_full_size(gpu, layout):
+    """The representative sequence (55,416 tokens) split over P=8 ranks of
+    6,927 tokens, C=4, 56 heads of 128 (head groups of 7): one rank's QKV
+    unpack against the oracle, into token-major [S][G][D] or head-major
+    [G][S][D] Q/K/V.  With eight ranks every head-major run crosses seven
+    rank boundaries, so the unpack's workgroup walk over (chunk, rank, head)
+    runs at a realistic size with many token tiles per block."""
+    import head_relayout_amd as vrl
+    import oracle
+    from tests.gpu_harness import assert_bits_equal, to_dev
+
+    P, C, S_l, H, D = 8, 4, 6927, 56, 128
+    G, S = H // P, P * S_l
+    n_qkv = 3 * S_l * H * D
+    say(f"[unpack-p8-{layout}] oracle")
+    recv = datagen.values(n_qkv, seed=8, stream=0)
+    want = [np.zeros((S, G, D), dtype=np.uint16) for _ in range(3)]
+    oracle.qkv_unpack(oracle.dims(P, C, S_l, H, D), recv, *want)
+    say(f"[unpack-p8-{layout}] device")
+    bf = dict(dtype=torch.bfloat16, device=gpu)
+    if layout == "dense":
+        outs = [torch.full((S, G, D), 0, **bf) for _ in range(3)]
+        views = outs
+    else:
+        outs = [torch.full((G, S, D), 0, **bf) for _ in range(3)]
+        views = [t.transpose(0, 1) for t in outs]
+    vrl.qkv_unpack(to_dev(recv, gpu), *views, P, C)
+    torch.cuda.synchronize()
+    for q in range(3):
+        assert_bits_equal(views[q], want[q], f"unpack P=8 {layout} plane {q}")
+    del outs, views
+    torch.cuda.empty_cache()
