@@ -17,12 +17,11 @@ FLAGS = [
 ]
 
 
-def build(out: str | None = None, defines: tuple = ()) -> str:
-    """Compiles the library; `defines` are extra -D macros (build-time tuning
-    knobs such as VRL_UNROLL), `out` an alternative output path."""
+def build(out: str | None = None) -> str:
+    """Compiles the library (`out`: an alternative output path)."""
     out = out or os.path.join(HERE, "libvrl.so")
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-o", tmp, *SOURCES]
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag; that warning is noise
     noise = "'-packed-fp32-ops' is not a recognized feature"

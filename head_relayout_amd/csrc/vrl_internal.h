@@ -10,44 +10,19 @@ namespace vrl {
 
 // Workgroup shape.  A workgroup moves one tile of kThreads * kUnroll vectors
 // of one wire block; each lane issues kUnroll independent loads before its
-// stores.  Tunable at build time.
-#ifndef VRL_THREADS
-#define VRL_THREADS 256
-#endif
-#ifndef VRL_UNROLL
-#define VRL_UNROLL 8
-#endif
-constexpr int kThreads = VRL_THREADS;
-constexpr int kUnroll = VRL_UNROLL;
+// stores.
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
 constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
 
-// Head-major views (a head's tokens closer together than a token's heads):
-// whether scatters into them (unpack, merge) and gathers from them (pack,
-// split) with head rows of at least VRL_HEADRUN_MIN_BYTES run as head runs
-// (headrun_kernel) rather than in wire order (relayout_kernel).
-#ifndef VRL_HEADRUN_SCATTER
-#define VRL_HEADRUN_SCATTER 1
-#endif
-#ifndef VRL_HEADRUN_GATHER
-#define VRL_HEADRUN_GATHER 0
-#endif
-// Whether gathers from head-major views with head rows narrower than
-// VRL_HEADRUN_MIN_BYTES go through the LDS transpose (else wire order).
-#ifndef VRL_STAGE_NARROW_GATHER
-#define VRL_STAGE_NARROW_GATHER 1
-#endif
-// Head rows (2*D bytes) narrower than this go through the LDS transpose
-// (staged_kernel) instead of head runs, when a tile of whole wire rows fits
-// the LDS budget.
-#ifndef VRL_HEADRUN_MIN_BYTES
-#define VRL_HEADRUN_MIN_BYTES 128
-#endif
+// Head-major views (a head's tokens closer together than a token's heads)
+// whose head rows (2*D bytes) are narrower than this go through the LDS
+// transpose (staged_kernel); scatters into head-major views with wider head
+// rows run as head runs (headrun_kernel), gathers from them in wire order.
+constexpr int64_t kHeadrunMinBytes = 128;
 // LDS budget of one workgroup of the staged kernel; a tile holds as many
-// tokens of its Gt heads as fit (rows padded by one vector).
-#ifndef VRL_LDS_BYTES
-#define VRL_LDS_BYTES 16384
-#endif
-constexpr uint32_t kLdsBytes = VRL_LDS_BYTES;
+// tokens of its Gt heads as fit.
+constexpr uint32_t kLdsBytes = 16384;
 
 enum class Op : int { Pack = 0, Unpack = 1, Split = 2, Merge = 3 };
 
@@ -80,7 +55,8 @@ struct KernelArgs {
     uint64_t gv_magic;         // staged kernel: i / (Gt * head_vecs)
     uint64_t tv_magic;         // staged kernel: i / (TT * head_vecs)
     uint32_t tv_shift;
-    uint32_t pad_;
+    uint32_t swz_shift;        // staged kernel: LDS column swizzle of token t is
+    uint32_t swz_mask;         //   ((t >> swz_shift) * head_vecs) & swz_mask
 };
 
 struct LaunchPlan {

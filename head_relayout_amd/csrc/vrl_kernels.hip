@@ -57,48 +57,18 @@ struct Vec<2> {
     typedef uint16_t type;
 };
 
-// Build-time knobs, kept so the measured alternatives can be rebuilt; the
-// defaults are the measured best at the representative shape.
-//   VRL_RANK_INNER   pack/merge workgroups rank-innermost (1) or outermost
-//   VRL_PLANE_INNER  pack workgroups plane-innermost after the rank
-//   VRL_CHUNK_INNER  head-chunked scatters chunk-innermost
-//   VRL_LOAD_NT / VRL_STORE_NT  non-temporal loads / stores
-#ifndef VRL_RANK_INNER
-#define VRL_RANK_INNER 1
-#endif
-#ifndef VRL_PLANE_INNER
-#define VRL_PLANE_INNER 0
-#endif
-#ifndef VRL_CHUNK_INNER
-#define VRL_CHUNK_INNER 1
-#endif
-
-// Streaming cache policy: every byte is touched exactly once.
-#ifndef VRL_LOAD_NT
-#define VRL_LOAD_NT 1
-#endif
-#ifndef VRL_STORE_NT
-#define VRL_STORE_NT 1
-#endif
-
+// Streaming cache policy: every byte is touched exactly once, so loads and
+// stores are non-temporal.
 template <typename V>
 __device__ __forceinline__ V load_vec(const V *p)
 {
-#if VRL_LOAD_NT
     return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
 }
 
 template <typename V>
 __device__ __forceinline__ void store_vec(V *p, V v)
 {
-#if VRL_STORE_NT
     __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
 }
 
 // n / d for n < 2^31, with magic = ceil(2^shift / d), shift = 31 + ceil(log2 d):
@@ -181,7 +151,7 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
     uint32_t plane = 0, tile, rest;
     int32_t c;
     int64_t p;
-    if (VRL_CHUNK_INNER && a.chunk_heads && !Tr::gather) {
+    if (a.chunk_heads && !Tr::gather) {
         // Scatters with head chunks: a view row is cut into C pieces (and P
         // pieces on the [S_l][H][D] side), so the chunk varies fastest, then
         // the rank, and the pieces of a row are written together.  (Gathers
@@ -204,24 +174,17 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
             }
             p = int64_t(rest);
         }
-    } else if (VRL_RANK_INNER && Tr::hside) {
+    } else if (Tr::hside) {
         // Pack and merge: the P head groups of one token row belong to
         // different ranks, so the rank varies fastest and neighbouring
         // workgroups cover whole rows of the [S_l][H][D] side together.
         p = int64_t(wg % uint32_t(a.P));
         rest = wg / uint32_t(a.P);
-        if (Tr::planes3 && VRL_PLANE_INNER) {
+        tile = rest % a.tiles;
+        rest /= a.tiles;
+        if (Tr::planes3) {
             plane = rest % 3u;
             rest /= 3u;
-            tile = rest % a.tiles;
-            rest /= a.tiles;
-        } else {
-            tile = rest % a.tiles;
-            rest /= a.tiles;
-            if (Tr::planes3) {
-                plane = rest % 3u;
-                rest /= 3u;
-            }
         }
         c = a.c_begin + int32_t(rest);
     } else {
@@ -363,11 +326,18 @@ __device__ __forceinline__ void decode_run(const KernelArgs &a, uint32_t rest, u
 // the group) whose head rows fill at least one 128-byte line of the wire
 // row, for a gather the whole group, so that it writes whole wire rows.  It
 // reads the tile in the source's contiguous order into LDS (laid out
-// [token][Gt heads], each LDS row padded by one vector so that the column
-// reads of the other phase spread over the banks), and after a barrier
-// writes it in the destination's contiguous order: runs of TT tokens per
-// head for a scatter, wire-row pieces for a gather.  Workgroups are ordered
-// as the head runs are (decode_run), token tile fastest.
+// [token][Gt heads]) and after a barrier writes it in the destination's
+// contiguous order: runs of TT tokens per head for a scatter, wire-row
+// pieces for a gather.  Workgroups are ordered as the head runs are
+// (decode_run), token tile fastest.
+//
+// LDS rows are not padded; instead the column of each vector is XORed with
+// a per-token swizzle ((t >> swz_shift) * head_vecs, masked to the largest
+// power of two dividing the row, at most one bank sweep of vectors).  The
+// view-order phase has a wave's lanes walk one head's column down
+// consecutive tokens; the swizzle moves consecutive tokens' head rows onto
+// different banks, while the wire-order phase, which walks along rows,
+// still sees a permutation of whole aligned groups of columns.
 template <Op OP, int VB>
 __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
 {
@@ -391,7 +361,6 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
     const uint32_t tte = uint32_t(min(int64_t(TT), b.T - t0));  // tokens in this tile
     const uint32_t hv = a.head_vecs;
     const uint32_t gv = a.group_heads * hv;                        // vectors of a tile row
-    const uint32_t lrow = gv + 1;                                  // padded LDS row
     const uint32_t nv = TT * gv;                                   // vectors of a full tile
     const int64_t st = b.st, sh = b.sh, row = int64_t(a.row_heads) * a.D;
     const uint32_t h0 = hg * a.group_heads;
@@ -404,17 +373,22 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
         uint32_t t, lds;
         int64_t off;  // element offset on the side being read or written
     };
+    // LDS slot of column j of token t (swz_mask + 1 divides gv, so the XOR
+    // stays inside the row)
+    auto slot = [&](uint32_t t, uint32_t j) -> uint32_t {
+        return t * gv + (j ^ (((t >> a.swz_shift) * hv) & a.swz_mask));
+    };
     auto wire_order = [&](uint32_t i) -> Pos {
         const uint32_t t = div_magic(i, a.gv_magic, a.gv_shift);
         const uint32_t j = i - t * gv;
-        return Pos{t, t * lrow + j, int64_t(t) * row + int64_t(j) * VE};
+        return Pos{t, slot(t, j), int64_t(t) * row + int64_t(j) * VE};
     };
     auto view_order = [&](uint32_t i) -> Pos {
         const uint32_t h = div_magic(i, a.tv_magic, a.tv_shift);
         const uint32_t r = i - h * (TT * hv);
         const uint32_t t = div_magic(r, a.head_magic, a.head_shift);
         const uint32_t e = r - t * hv;
-        return Pos{t, t * lrow + h * hv + e, int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
+        return Pos{t, slot(t, h * hv + e), int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
     };
 
     // Phase 1: source -> LDS, in the source's contiguous order.

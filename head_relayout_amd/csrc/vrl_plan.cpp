@@ -121,12 +121,12 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     // heads per LDS-transpose tile: a gather writes whole wire rows (all Gb
     // heads, one write stream), a scatter the fewest heads that fill a line
     const int64_t gt = gather ? Gb : staged_heads(Gb, d->D);
-    const bool narrow = d->D * 2 < VRL_HEADRUN_MIN_BYTES && (gt * a.head_vecs + 1) * vb <= int64_t(kLdsBytes);
+    const bool narrow = d->D * 2 < kHeadrunMinBytes && gt * a.head_vecs * vb <= int64_t(kLdsBytes);
     int64_t tiles = a.tiles;
     if (!head_major || Gb <= 1) {
         // token-major (or one head per row): wire order (direct kernel)
-    } else if (narrow && (gather ? VRL_STAGE_NARROW_GATHER : VRL_HEADRUN_SCATTER)) {
-        const int64_t lrow_bytes = (gt * a.head_vecs + 1) * vb;
+    } else if (narrow) {
+        const int64_t lrow_bytes = gt * a.head_vecs * vb;
         // tokens per tile: as many as fit, rounded to whole lines of a head's run
         const int64_t quantum = std::max<int64_t>(1, 128 / (d->D * 2));
         int64_t tt = int64_t(kLdsBytes) / lrow_bytes;
@@ -138,9 +138,21 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
         a.tok_tiles = uint32_t((t_max + tt - 1) / tt);
         magic_for(uint32_t(gt * a.head_vecs), a.gv_magic, a.gv_shift);
         magic_for(uint32_t(tt * a.head_vecs), a.tv_magic, a.tv_shift);
+        // LDS column swizzle: g = the largest power of two dividing the row
+        // (in vectors), at most one sweep of the 64 four-byte banks; rows
+        // t and t + sweep/g start on the same bank, so the swizzle changes
+        // every sweep/g tokens.
+        const int64_t sweep = 256 / vb;
+        int64_t g = 1;
+        while (g < sweep && (gt * a.head_vecs) % (2 * g) == 0)
+            g *= 2;
+        a.swz_mask = uint32_t(g - 1);
+        a.swz_shift = 0;
+        while ((int64_t(1) << a.swz_shift) < sweep / g)
+            ++a.swz_shift;
         pl.lds_bytes = uint32_t(tt * lrow_bytes);
         tiles = (Gb / gt) * int64_t(a.tok_tiles);
-    } else if ((gather ? VRL_HEADRUN_GATHER : VRL_HEADRUN_SCATTER) && a.head_vecs <= kTileVecs) {
+    } else if (!gather && a.head_vecs <= kTileVecs) {
         const int64_t tt = std::min<int64_t>(kTileVecs / a.head_vecs, t_max);
         pl.headrun = true;
         a.tile_tokens = uint32_t(tt);

@@ -73,9 +73,14 @@ bool run(const Case &k)
         ok = ok && pl.args.group_heads == uint32_t(k.gt);
     if (k.grid)
         ok = ok && pl.grid == uint32_t(k.grid);
-    if (got == STAGED)  // the LDS tile fits the budget and holds whole padded rows
-        ok = ok && pl.lds_bytes <= kLdsBytes &&
-             pl.lds_bytes == pl.args.tile_tokens * (pl.args.group_heads * pl.args.head_vecs + 1) * uint32_t(pl.vec_bytes);
+    if (got == STAGED) {  // the LDS tile fits the budget and holds whole rows
+        const uint32_t gv = pl.args.group_heads * pl.args.head_vecs;
+        ok = ok && pl.lds_bytes <= kLdsBytes && pl.lds_bytes == pl.args.tile_tokens * gv * uint32_t(pl.vec_bytes);
+        // the column swizzle is a power-of-two mask dividing the row, so it
+        // permutes columns within the row
+        const uint32_t m = pl.args.swz_mask;
+        ok = ok && (m & (m + 1)) == 0 && gv % (m + 1) == 0 && (m + 1) * uint32_t(pl.vec_bytes) <= 256;
+    }
     std::printf("%-44s %-8s vb=%2d tt=%5u gt=%2u grid=%8u lds=%5u %s\n", k.what, name(got), pl.vec_bytes,
                 got == DIRECT ? 0u : pl.args.tile_tokens, got == STAGED ? pl.args.group_heads : 0u, pl.grid,
                 pl.lds_bytes, ok ? "ok" : "UNEXPECTED");
@@ -100,15 +105,15 @@ int main()
         {"pack from head-major, D=128", Op::Pack, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 36384, 16},
         {"unpack into head-major, head chunks", Op::Unpack, 2, 4, R, 56, 128, 1, true, 0, HEADRUN, 128, 0, 0, 16},
         {"unpack into head-major, D=64", Op::Unpack, 2, 4, 2 * R, 56, 64, 0, true, 0, HEADRUN, 256, 0, 0, 16},
-        // 126-byte head rows: 2 heads fill a line; (2*63 + 1) 2-byte vectors per LDS row
+        // 126-byte head rows: 2 heads fill a line; 2*63 2-byte vectors per LDS row
         {"unpack into head-major, D=63", Op::Unpack, 2, 3, 20, 4, 63, 0, true, 0, STAGED, 7, 2, 0, 2},
-        // 4 heads x 32 B fill a line; 9 vectors per LDS row -> 113 tokens, rounded to 112
-        {"unpack into head-major, D=16", Op::Unpack, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
-        {"merge into head-major, D=16", Op::Merge, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 112, 4, 0, 16},
-        {"unpack into head-major, D=32", Op::Unpack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 112, 2, 0, 16},
-        // gathers: whole wire rows (28 heads); 57 vectors per LDS row -> 17 tokens, rounded to 16
+        // 4 heads x 32 B fill a line; 8 vectors per LDS row -> 128 tokens
+        {"unpack into head-major, D=16", Op::Unpack, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 128, 4, 0, 16},
+        {"merge into head-major, D=16", Op::Merge, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 128, 4, 0, 16},
+        {"unpack into head-major, D=32", Op::Unpack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 128, 2, 0, 16},
+        // gathers: whole wire rows (28 heads); 56 vectors per LDS row -> 18 tokens, rounded to 16
         {"split from head-major, D=16", Op::Split, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 16, 28, 0, 16},
-        // 113 vectors per LDS row -> 9 tokens, rounded to 8
+        // 112 vectors per LDS row -> 9 tokens, rounded to 8
         {"pack from head-major, D=32", Op::Pack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 8, 28, 0, 16},
         {"unpack into head-major, D=8, 5 heads", Op::Unpack, 2, 4, 64, 10, 8, 0, true, 0, STAGED, 0, 5, 0, 16},
         {"unpack into head-major, one head per group", Op::Unpack, 2, 4, 64, 2, 128, 0, true, 0, DIRECT, 0, 0, 0, 16},
