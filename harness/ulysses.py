@@ -69,14 +69,23 @@ class Layer:
     """Shapes and per-chunk wire offsets of P ranks' Ulysses exchange.
 
     engine: how the stand-in exchange copies blocks inside the one HBM --
-    "kernel" (torch copies, run as copy kernels on the compute units) or
-    "sdma" (hipMemcpyAsync on the copy engines, no compute units).  A real
-    run moves the blocks over xGMI with RCCL instead."""
+    "kernel" (torch copies, run as copy kernels on the compute units),
+    "sdma" (hipMemcpyAsync on the copy engines, no compute units) or "link"
+    (one copy kernel per chunk that paces every block between two distinct
+    ranks to link_gbs, each pair on a link of its own; harness/linkmodel.py).
+    A real run moves the blocks over xGMI with RCCL instead."""
 
-    def __init__(self, P: int, C: int, s_local: int, H: int, D: int, engine: str = "kernel"):
-        if engine not in ("kernel", "sdma"):
+    def __init__(self, P: int, C: int, s_local: int, H: int, D: int, engine: str = "kernel",
+                 link_gbs: float | None = None):
+        if engine not in ("kernel", "sdma", "link"):
             raise ValueError(f"unknown exchange engine {engine!r}")
+        if engine == "link" and P * P > 64:
+            raise ValueError("the link-paced exchange takes at most 8 ranks")
         self.engine = engine
+        if link_gbs is None:
+            from harness.linkmodel import XGMI_LINK_GBS
+            link_gbs = XGMI_LINK_GBS
+        self.link_gbs = link_gbs
         self.P, self.C, self.s_local, self.H, self.D = P, C, s_local, H, D
         self.G = H // P
         self.off = [vrl.chunk_offset(c, P, C, s_local, H, D) for c in range(C + 1)]
@@ -92,6 +101,11 @@ class Layer:
         per_token = (3 if qkv else 1) * self.G * self.D
         stream = torch.cuda.current_stream().cuda_stream
         for c in (range(self.C) if chunks is None else chunks):
+            if self.engine == "link":
+                from harness import linkmodel
+                linkmodel.exchange([(sends[s][self.block(r, c, per_token)], recvs[r][self.block(s, c, per_token)],
+                                     s != r) for s in range(self.P) for r in range(self.P)], self.link_gbs)
+                continue
             for s in range(self.P):
                 for r in range(self.P):
                     dst = recvs[r][self.block(s, c, per_token)]
@@ -103,6 +117,15 @@ class Layer:
                                                       _HIP_MEMCPY_D2D_NO_CU, stream)
                     if rc != 0:
                         raise RuntimeError(f"hipMemcpyAsync failed with HIP error {rc}")
+
+
+def run_exchanges(layer: Layer, ranks) -> None:
+    """Only the layer's exchanges, chunk by chunk on the current stream (QKV,
+    then the return path): the time the exchange alone takes."""
+    for c in range(layer.C):
+        layer.exchange([rk.packed for rk in ranks], [rk.recv for rk in ranks], True, [c])
+    for c in range(layer.C):
+        layer.exchange([rk.send for rk in ranks], [rk.back for rk in ranks], False, [c])
 
 
 def run_serial(layer: Layer, ranks, plane: int = 0) -> None:
