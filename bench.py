@@ -80,12 +80,14 @@ def parse_args():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed step: skip the overlap, head-chunk, head-major and "
                          "reference sections (for profiler runs)")
-    ap.add_argument("--mode", choices=["bench", "pmc", "pmc-sq"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "windows", "pmc", "pmc-sq"], default="bench")
     ap.add_argument("--reps", type=int, default=10, help="launches per kernel in --mode pmc")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output trees (FETCH_SIZE, WRITE_SIZE)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats output tree")
+    ap.add_argument("--windows-summary", metavar="DIR",
+                    help="summarise the window launches of a kernel trace of --mode windows")
     ap.add_argument("--sq-summary", metavar="DIR",
                     help="summarise a rocprofv3 --pmc output tree of SQ counters per kernel")
     return ap.parse_args()
@@ -260,11 +262,14 @@ def run_bench(args):
                              "ms_median": round(ms, 5),
                              "gbs": round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)}
         del dst
+    say("[bench] copy ceiling: the library's copy core on a plain contiguous relayout")
+    ceiling = copy_ceiling(torch, vrl, w)
     for name in per_op:
         key = "qkv" if name in ("qkv_pack", "qkv_unpack") else "attn"
         per_op[name]["pct_of_d2d_copy"] = round(100 * per_op[name]["gbs"] / copies[key]["gbs"], 1)
         med_gbs = nbytes[name] / (per_op[name]["ms_median"] * 1e-3) / 1e9   # medians on both sides
         per_op[name]["pct_of_elementwise_copy"] = round(100 * med_gbs / elementwise[key]["gbs"], 1)
+        per_op[name]["pct_of_copy_ceiling"] = round(100 * med_gbs / ceiling["gbs"], 1)
 
     dominant = "qkv_pack"
     achieved = per_op[dominant]["gbs"]
@@ -295,6 +300,7 @@ def run_bench(args):
         "roofline": roofline,
         "copy_d2d": copies,
         "copy_elementwise": elementwise,
+        "copy_ceiling": ceiling,
         "verified": "round trip bit-exact before and after timing",
         "kernel_sources": kernel_source_hash(),
     }
@@ -303,9 +309,14 @@ def run_bench(args):
     if not round_trip_ok():
         raise SystemExit("round trip is not bit-exact after graph replays")
     if not args.no_extras:
+        say("[bench] one-chunk windows")
+        result["windows"] = chunk_windows(torch, vrl, w, ranks)
         say("[bench] four-chunk overlap schedule")
-        result["overlap"] = overlap_schedule(torch, w, ranks)
-        result["overlap_sdma"] = overlap_schedule(torch, w, ranks, engine="sdma")
+        kernels_ms = round(P * sum(per_op[n]["ms"] for n in per_op), 4)
+        result["overlap"] = overlap_schedule(torch, w, ranks, kernels_ms=kernels_ms)
+        result["overlap_sdma"] = overlap_schedule(torch, w, ranks, engine="sdma", kernels_ms=kernels_ms)
+        say("[bench] four-chunk overlap schedule, link-paced exchange")
+        result["overlap_link_model"] = overlap_schedule(torch, w, ranks, engine="link", kernels_ms=kernels_ms)
         say("[bench] head-chunked layout")
         result["head_chunks"] = head_chunk_layout(torch, vrl, w, ranks)
         say("[bench] head-major (BHTD) attention side")
@@ -320,62 +331,127 @@ def run_bench(args):
             result["smaller_workloads"] = smaller_workloads(torch, np, datagen, vrl, dev)
     if not args.no_reference and not args.no_extras:
         say("[bench] reference materialisation arm (A/direct/A)")
-        result["reference_arm"] = reference_arm(torch, vrl, w, ranks[0])
+        result["reference_arm"] = reference_arm(torch, vrl, w, ranks)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, [rk.host for rk in ranks], nbytes)
     print(json.dumps(result), flush=True)
 
 
-# ---- the reference materialisation chains on the GPU (comparison arm) ----------
+# ---- timing helpers -------------------------------------------------------------
 
-def ref_pack(torch, q, k, v, P, C):
-    """stack, then each (dest, chunk) block copied into its slot of a new buffer:
-    two materialisations, as in the pages' reference chain."""
-    S_l, H, D = q.shape
-    X = torch.stack([q, k, v], 0)
-    Xv = X.view(3, S_l, P, H // P, D)
-    out = torch.empty(3 * S_l * H * D, dtype=q.dtype, device=q.device)
-    at = 0
-    for d in range(P):
-        for blk in torch.tensor_split(Xv[:, :, d], C, dim=1):
-            n = blk.numel()
-            out[at:at + n].view(blk.shape).copy_(blk)
-            at += n
+def _queued(torch, fn, sets, reps):
+    """fn(set) called `reps` times, cycling through `sets`, queued back to
+    back on the current stream with no host synchronisation in between, in
+    two passes: one with HIP events around every call (sorted per-call times)
+    and one with events only around the whole queue (mean per call, the
+    queue's throughput without the per-call events).  Times in ms.
+    Whatever fn returns is dropped as soon as it is queued, so a chain's own
+    allocations are recycled by torch's allocator."""
+    pairs = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = fn(sets[i % len(sets)])
+        e1.record()
+        del out
+        pairs.append((e0, e1))
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record()
+    for i in range(reps):
+        out = fn(sets[i % len(sets)])
+        del out
+    q1.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in pairs), q0.elapsed_time(q1) / reps
+
+
+def _stats(ts, mean=None, nbytes=None) -> dict:
+    n = len(ts)
+    out = {"ms_median": round(ts[n // 2], 5), "ms_p10": round(ts[n // 10], 5),
+           "ms_p90": round(ts[(9 * n) // 10], 5), "launches": n}
+    if mean is not None:
+        out["ms_mean_queued"] = round(mean, 5)
+    if nbytes is not None:
+        gbs = nbytes / (ts[n // 2] * 1e-3) / 1e9
+        out.update({"bytes": nbytes, "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)})
     return out
 
 
-def ref_unpack(torch, recv, P, C, S_l, G, D):
-    """per plane, cat of the received blocks: one materialisation."""
-    lens = [len(x) for x in torch.tensor_split(torch.arange(S_l), C)]
-    blocks = torch.split(recv, [3 * T * G * D for _ in range(P) for T in lens])
-    shaped = [b.view(3, T, G, D) for b, T in zip(blocks, lens * P)]
-    return [torch.cat([b[q] for b in shaped], 0) for q in range(3)]
+def _sets_for(nbytes: int, have: int) -> int:
+    """Buffer sets to rotate so that k x bytes per launch >= 1 GiB (the 256 MB
+    Infinity Cache then holds none of a launch's inputs), at most `have`."""
+    return max(1, min(have, -(-(1 << 30) // nbytes)))
 
 
-def ref_split(torch, o, P, C, c_begin=0, c_end=None):
-    """cat of each (dest, chunk) token slice of O: one materialisation."""
-    S, G, D = o.shape
-    Ov = o.view(P, S // P, G, D)
-    parts = []
-    for d in range(P):
-        chunks = torch.tensor_split(Ov[d], C, 0)
-        parts += [x.reshape(-1) for x in chunks[c_begin:c_end]]
-    return torch.cat(parts)
+# ---- the reference materialisation chains on the GPU (comparison arm) ----------
 
+def reference_arm(torch, vrl, w, ranks, reps=16):
+    """A/direct/A of the reference chains (harness/reference_chains.py)
+    against the direct relayouts, and their incremental peak allocations.
+    Each arm's calls are queued back to back, so the GPU times hold neither
+    the binding's host cost nor idle gaps; inputs rotate over enough buffers
+    that every call reads from HBM; the direct calls write into outputs
+    allocated beforehand, while the chains allocate theirs as they go (that
+    is what they do; torch's allocator recycles them, no device allocation
+    happens in the timed region)."""
+    from harness import reference_chains as rc
 
-def ref_merge(torch, recv, P, S_l, G, D):
-    """stack of the per-source head groups, then permute + contiguous: two
-    materialisations."""
-    Y = torch.stack([recv.view(P, S_l, G, D)[s] for s in range(P)], 0)
-    return Y.permute(1, 0, 2, 3).contiguous().view(S_l, P * G, D)
-
-
-def reference_arm(torch, vrl, w, rk):
-    """A/direct/A medians and incremental peak allocations of the reference
-    chains against the direct relayouts, on rank 0's buffers."""
     P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
-    bf = dict(dtype=torch.bfloat16, device=rk.fused.device)
+    bf = dict(dtype=torch.bfloat16, device=ranks[0].fused.device)
     T0 = vrl.chunk_offset(1, P, C, S_l, H, D)
+    nb = op_bytes(w)
+    packed_out = torch.empty_like(ranks[0].packed)
+    planes_out = [torch.empty(S, G, D, **bf) for _ in range(3)]
+    send_out = torch.empty_like(ranks[0].send)
+    merged_out = torch.empty(S_l, H, D, **bf)
+    qkv_sets = [rk.qkv for rk in ranks]
+    recv_sets = [rk.recv for rk in ranks]
+    o_sets = [p for rk in ranks for p in rk.planes]
+    ret_sets = [t for rk in ranks for t in (rk.back, rk.send)]
+    one_chunk = 2 * P * T0 * G * D * 2
+    arms = {
+        "qkv_pack": (qkv_sets, nb["qkv_pack"], lambda x: rc.ref_pack(torch, *x, P, C),
+                     lambda x: vrl.qkv_pack(*x, packed_out, P, C), lambda: packed_out),
+        "qkv_unpack": (recv_sets, nb["qkv_unpack"], lambda x: rc.ref_unpack(torch, x, P, C, S_l, G, D),
+                       lambda x: vrl.qkv_unpack(x, *planes_out, P, C), lambda: planes_out),
+        "attn_split": (o_sets, nb["attn_split"], lambda x: rc.ref_split(torch, x, P, C),
+                       lambda x: vrl.attn_split(x, send_out, P, C), lambda: send_out),
+        "attn_split_one_chunk": (o_sets, one_chunk, lambda x: rc.ref_split(torch, x, P, C, 0, 1),
+                                 lambda x: vrl.attn_split(x, send_out, P, C, 0, 1),
+                                 lambda: send_out.view(P, S_l * G * D)[:, :T0 * G * D]),
+        "head_merge": (ret_sets, nb["head_merge"], lambda x: rc.ref_merge(torch, x, P, S_l, G, D),
+                       lambda x: vrl.head_merge(x, merged_out, P, C), lambda: merged_out),
+    }
+    res = {}
+    for name, (sets, nbytes, ref_fn, dir_fn, dir_out) in arms.items():
+        k = _sets_for(nbytes, len(sets))
+        sets = sets[:k]
+        # bit-exact agreement of the two arms on the first set
+        a = ref_fn(sets[0])
+        dir_fn(sets[0])
+        b = dir_out()
+        a = a if isinstance(a, list) else [a]
+        b = b if isinstance(b, list) else [b]
+        for x, y in zip(a, b):
+            if not torch.equal(x.reshape(-1).view(torch.int16), y.reshape(-1).view(torch.int16)):
+                raise SystemExit(f"reference and direct {name} differ")
+        del a, b
+        for fn in (ref_fn, dir_fn):      # warm-up: each set once
+            for x in sets:
+                fn(x)
+        ra, ra_mean = _queued(torch, ref_fn, sets, reps)
+        dm, dm_mean = _queued(torch, dir_fn, sets, reps)
+        rb, rb_mean = _queued(torch, ref_fn, sets, reps)
+        ref_med = (ra[len(ra) // 2] + rb[len(rb) // 2]) / 2
+        entry = {"reference": _stats(ra + rb, (ra_mean + rb_mean) / 2), "direct": _stats(dm, dm_mean),
+                 "reference_ms": round(ref_med, 5), "direct_ms": round(dm[len(dm) // 2], 5),
+                 "speedup": round(ref_med / dm[len(dm) // 2], 3), "bytes": nbytes, "buffer_sets": k}
+        if name == "attn_split_one_chunk":
+            entry["output_bytes"] = P * T0 * G * D * 2
+            entry["reference_peak_bytes"] = rc.peak_bytes(torch, lambda: ref_fn(sets[0]))
+        res[name] = entry
+    # incremental peak allocations: each arm with an output of its own
+    rk = ranks[0]
 
     def d_pack():
         out = torch.empty(rk.packed.numel(), **bf)
@@ -397,79 +473,89 @@ def reference_arm(torch, vrl, w, rk):
         vrl.head_merge(rk.back, out, P, C)
         return out
 
-    arms = {
-        "qkv_pack": (lambda: ref_pack(torch, *rk.qkv, P, C), d_pack),
-        "qkv_unpack": (lambda: ref_unpack(torch, rk.recv, P, C, S_l, G, D), d_unpack),
-        "attn_split": (lambda: ref_split(torch, rk.planes[0], P, C), d_split),
-        "head_merge": (lambda: ref_merge(torch, rk.back, P, S_l, G, D), d_merge),
-    }
-    res = {}
-    for name, (ref_fn, dir_fn) in arms.items():
-        # bit-exact agreement of the two arms
-        a, b = ref_fn(), dir_fn()
-        a = a if isinstance(a, list) else [a]
-        b = b if isinstance(b, list) else [b]
-        for x, y in zip(a, b):
-            if not torch.equal(x.reshape(-1).view(torch.int16), y.reshape(-1).view(torch.int16)):
-                raise SystemExit(f"reference and direct {name} differ")
-        del a, b
-
-        def peak(fn):
-            torch.cuda.synchronize()
-            base = torch.cuda.memory_allocated()
-            torch.cuda.reset_peak_memory_stats()
-            out = fn()
-            torch.cuda.synchronize()
-            p = torch.cuda.max_memory_allocated() - base
-            del out
-            return p
-
-        def med(fn, reps=7):
-            ts = []
-            for _ in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                out = fn()
-                e1.record()
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-                del out
-            return sorted(ts)[reps // 2]
-
-        for _ in range(2):
-            ref_fn(), dir_fn()
-        ra = med(ref_fn)
-        dm = med(dir_fn)
-        rb = med(ref_fn)
-        res[name] = {"reference_ms": round((ra + rb) / 2, 4), "direct_ms": round(dm, 4),
-                     "speedup": round((ra + rb) / 2 / dm, 3),
-                     "reference_peak_bytes": peak(ref_fn), "direct_peak_bytes": peak(dir_fn)}
-    # one-chunk split window (the pages' split figure is per chunk)
-    ref_c = lambda: ref_split(torch, rk.planes[0], P, C, 0, 1)
-
-    def dir_c():
-        out = torch.empty(rk.send.numel(), **bf)
-        vrl.attn_split(rk.planes[0], out, P, C, 0, 1)
-        return out
-    for _ in range(2):
-        ref_c(), dir_c()
-    ts = {}
-    for arm, fn in (("a", ref_c), ("b", dir_c), ("a2", ref_c)):
-        xs = []
-        for _ in range(7):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            out = fn()
-            e1.record()
-            torch.cuda.synchronize()
-            xs.append(e0.elapsed_time(e1))
-            del out
-        ts[arm] = sorted(xs)[3]
-    res["attn_split_one_chunk"] = {"reference_ms": round((ts["a"] + ts["a2"]) / 2, 4),
-                                   "direct_ms": round(ts["b"], 4),
-                                   "speedup": round((ts["a"] + ts["a2"]) / 2 / ts["b"], 3),
-                                   "output_bytes": P * T0 * G * D * 2}
+    for name, ref_fn, dir_fn in (
+            ("qkv_pack", lambda: rc.ref_pack(torch, *rk.qkv, P, C), d_pack),
+            ("qkv_unpack", lambda: rc.ref_unpack(torch, rk.recv, P, C, S_l, G, D), d_unpack),
+            ("attn_split", lambda: rc.ref_split(torch, rk.planes[0], P, C), d_split),
+            ("head_merge", lambda: rc.ref_merge(torch, rk.back, P, S_l, G, D), d_merge)):
+        res[name]["reference_peak_bytes"] = rc.peak_bytes(torch, ref_fn)
+        res[name]["direct_peak_bytes"] = rc.peak_bytes(torch, dir_fn)
+    del packed_out, planes_out, send_out, merged_out
     return res
+
+
+def chunk_windows(torch, vrl, w, ranks, reps=24):
+    """One-chunk windows [c, c+1) of the four relayouts, c = 0 .. C-1 (token
+    chunks), nothing else running: per-launch HIP events of calls queued
+    back to back over k buffer sets (k x window bytes >= 1 GiB, so every
+    launch reads from HBM), and the mean per launch of the whole queue.  The
+    windows composed over every chunk are checked equal to the whole call."""
+    P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
+    bf = dict(dtype=torch.bfloat16, device=ranks[0].fused.device)
+    off = [vrl.chunk_offset(c, P, C, S_l, H, D) for c in range(C + 1)]
+    n_att = S_l * H * D
+    res = {}
+    for name in ("qkv_pack", "qkv_unpack", "attn_split", "head_merge"):
+        planes3 = name in ("qkv_pack", "qkv_unpack")
+        win_bytes = [2 * (3 if planes3 else 1) * (off[c + 1] - off[c]) * H * D * 2 for c in range(C)]
+        k = _sets_for(min(win_bytes), 6)
+        if name == "qkv_pack":
+            ins = [rk.qkv for rk in ranks]
+            outs = [torch.empty_like(ranks[0].packed) for _ in range(k)]
+            call = lambda i, o, cb, ce: vrl.qkv_pack(*i, o, P, C, cb, ce)  # noqa: E731
+        elif name == "qkv_unpack":
+            ins = [rk.recv for rk in ranks]
+            outs = [[torch.empty(S, G, D, **bf) for _ in range(3)] for _ in range(k)]
+            call = lambda i, o, cb, ce: vrl.qkv_unpack(i, *o, P, C, cb, ce)  # noqa: E731
+        elif name == "attn_split":
+            ins = [p for rk in ranks for p in rk.planes]
+            outs = [torch.empty(n_att, **bf) for _ in range(k)]
+            call = lambda i, o, cb, ce: vrl.attn_split(i, o, P, C, cb, ce)  # noqa: E731
+        else:
+            ins = [t for rk in ranks for t in (rk.back, rk.send, rk.packed[:n_att])]
+            outs = [torch.empty(S_l, H, D, **bf) for _ in range(k)]
+            call = lambda i, o, cb, ce: vrl.head_merge(i, o, P, C, cb, ce)  # noqa: E731
+        sets = [(ins[j % len(ins)], outs[j]) for j in range(k)]
+        entry = {"buffer_sets": k}
+        for c in range(C):
+            for st in sets:
+                call(*st, c, c + 1)
+            ts, mean = _queued(torch, lambda st, c=c: call(*st, c, c + 1), sets, reps)
+            entry[f"chunk_{c}"] = _stats(ts, mean, win_bytes[c])
+        # composed windows == whole call (set 0's output holds every window now)
+        whole = (torch.empty_like(outs[0]) if not isinstance(outs[0], list)
+                 else [torch.empty_like(t) for t in outs[0]])
+        call(sets[0][0], whole, 0, C)
+        torch.cuda.synchronize()
+        a = outs[0] if isinstance(outs[0], list) else [outs[0]]
+        b = whole if isinstance(whole, list) else [whole]
+        if not all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(a, b)):
+            raise SystemExit(f"{name}: the one-chunk windows composed differ from the whole call")
+        res[name] = entry
+        del outs, sets, whole, a, b
+    return res
+
+
+def copy_ceiling(torch, vrl, w, reps=20):
+    """The library's direct kernel on a relayout that is a plain contiguous
+    copy: a QKV pack with P = 1 and C = 1 from three dense [S_l][H][D]
+    tensors (each plane one contiguous block), moving the pack's bytes.  What
+    the same copy core reaches without any index swap."""
+    S_l, H, D = w.s_local, w.H, w.D
+    dev = torch.device("cuda:0")
+    qkv = [torch.empty(S_l, H, D, dtype=torch.int16, device=dev).random_(-30000, 30000).view(torch.bfloat16)
+           for _ in range(3)]
+    out = torch.empty(3 * S_l * H * D, dtype=torch.bfloat16, device=dev)
+    fn = lambda _: vrl.qkv_pack(*qkv, out, 1, 1)  # noqa: E731
+    for _ in range(3):
+        fn(None)
+    ts, mean = _queued(torch, fn, [None], reps)
+    if not torch.equal(out.view(torch.int16), torch.cat([t.reshape(-1) for t in qkv]).view(torch.int16)):
+        raise SystemExit("copy ceiling: the P = 1 pack is not a plain copy")
+    entry = _stats(ts, mean, op_bytes(w)["qkv_pack"])
+    entry["kernel"] = "relayout_kernel<Pack, 16 B, contiguous> with P = 1, C = 1 (three contiguous copies)"
+    del qkv, out
+    return entry
 
 
 def graph_replay(torch, ops, ranks, step_bytes, steps):
@@ -503,20 +589,27 @@ def graph_replay(torch, ops, ranks, step_bytes, steps):
             "steps": steps}
 
 
-def overlap_schedule(torch, w, ranks, reps=10, engine="kernel"):
-    """The whole layer, exchanges included: serial (each stage over all
-    chunks, one after the other) against the four-chunk overlap schedule
-    (per-chunk stages, exchanges on a second stream, event-ordered ready
-    waits).  Exchanges are device copies in one HBM here -- copy kernels or
-    SDMA copies (engine) -- so they compete with the kernels for bandwidth
-    (and, as kernels, for compute units); on several GPUs they would use the
-    links instead."""
-    from harness.ulysses import Layer, run_overlapped, run_serial
+def overlap_schedule(torch, w, ranks, reps=10, engine="kernel", kernels_ms=None):
+    """The whole layer, exchanges included: the exchanges alone, the serial
+    schedule (each stage over all chunks, one after the other) and the
+    four-chunk overlap schedule (per-chunk stages, exchanges on a second
+    stream, event-ordered ready waits).  engine picks the stand-in exchange
+    (harness/ulysses.py): copy kernels or SDMA copies inside the one HBM,
+    which compete with the relayouts for bandwidth, or link-paced copies,
+    which take each block between two ranks at one xGMI link's rate and so
+    cost the HBM only what the links would carry.  exposed_* = schedule time
+    minus the exchanges alone: the relayout time the schedule leaves
+    uncovered.  kernels_ms: the layer's relayouts alone (every rank's four
+    calls, from the timed step)."""
+    from harness.ulysses import Layer, run_exchanges, run_overlapped, run_serial
 
     layer = Layer(w.P, w.C, w.s_local, w.H, w.D, engine)
     comm = torch.cuda.Stream()
     out = {"exchange": engine}
-    for name, fn in (("serial", lambda: run_serial(layer, ranks)),
+    if engine == "link":
+        out["link_gbs"] = layer.link_gbs
+    for name, fn in (("exchanges_only", lambda: run_exchanges(layer, ranks)),
+                     ("serial", lambda: run_serial(layer, ranks)),
                      ("overlapped", lambda: run_overlapped(layer, ranks, comm))):
         for _ in range(2):
             fn()
@@ -526,13 +619,17 @@ def overlap_schedule(torch, w, ranks, reps=10, engine="kernel"):
             fn()
         torch.cuda.synchronize()
         out[name + "_ms"] = round(1e3 * (time.perf_counter() - t0) / reps, 4)
+    out["exposed_serial_ms"] = round(out["serial_ms"] - out["exchanges_only_ms"], 4)
+    out["exposed_overlapped_ms"] = round(out["overlapped_ms"] - out["exchanges_only_ms"], 4)
+    if kernels_ms is not None:
+        out["kernels_ms"] = kernels_ms
     waits = {}
     run_overlapped(layer, ranks, comm, waits=waits)
     torch.cuda.synchronize()
     for kind, pairs in waits.items():
         out[kind + "_ready_wait_ms"] = round(sum(a.elapsed_time(b) for a, b in pairs), 4)
     if not all(torch.equal(rk.merged.view(torch.int16), rk.qkv[0].view(torch.int16)) for rk in ranks):
-        raise SystemExit("overlap schedule: round trip is not bit-exact")
+        raise SystemExit(f"overlap schedule ({engine} exchange): round trip is not bit-exact")
     out["chunks"] = w.C
     return out
 
@@ -589,8 +686,15 @@ def head_chunk_layout(torch, vrl, w, ranks):
         ms = _median_ms(torch, fn)
         gbs = nb[name] / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
-    ms = _median_ms(torch, lambda: vrl.attn_split(planes[0][0], send[0], P, C, 0, 1, **hc))
-    out["attn_split_one_chunk"] = {"ms": round(ms, 5), "output_bytes": S * (G // C) * D * 2}
+    # one chunk window, rotating over every plane of every rank (and as many
+    # outputs) so that each launch reads from HBM
+    one = 2 * S * (G // C) * D * 2
+    sets = [(planes[r][q], send[r]) for r in range(P) for q in range(3)][:_sets_for(one, 3 * P)]
+    for o, sd in sets:
+        vrl.attn_split(o, sd, P, C, 0, 1, **hc)
+    ts, mean = _queued(torch, lambda st: vrl.attn_split(st[0], st[1], P, C, 0, 1, **hc), sets, 24)
+    out["attn_split_one_chunk"] = _stats(ts, mean, one)
+    out["attn_split_one_chunk"]["output_bytes"] = S * (G // C) * D * 2
     return out
 
 
@@ -896,6 +1000,29 @@ def kernel_label(name):
     return op, "direct"
 
 
+def run_windows(args):
+    """Only the one-chunk windows section, for a kernel trace of its own."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import head_relayout_amd as vrl
+
+    dev = torch.device("cuda:0")
+    w = datagen.WORKLOADS[args.workload]
+    say(f"[windows] workload {w.cid} ({w.name}): inputs for {w.P} ranks")
+    ranks = [Rank(w, r, dev, torch, np, datagen, vrl) for r in range(w.P)]
+    for rk in ranks:
+        vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
+    exchange([rk.packed for rk in ranks], [rk.recv for rk in ranks], w.P)
+    for rk in ranks:
+        vrl.qkv_unpack(rk.recv, *rk.planes, w.P, w.C)
+        vrl.attn_split(rk.planes[0], rk.send, w.P, w.C)
+    exchange([rk.send for rk in ranks], [rk.back for rk in ranks], w.P)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": w.name, "windows": chunk_windows(torch, vrl, w, ranks)}), flush=True)
+
+
 def run_pmc(args):
     """Every relayout kernel the representative shape uses (the four
     token-major ones, the head-run scatters into head-major views and the split
@@ -941,9 +1068,11 @@ def run_pmc(args):
 
 def run_pmc_sq(args):
     """The head-run unpack into head-major Q/K/V, the direct unpack into
-    token-major ones and the pack, then the LDS-transpose unpack into
-    head-major Q/K/V of 16-element heads (221,656 tokens per rank, the same
-    bytes), `reps` launches each, for SQ counter runs."""
+    token-major ones and the pack, then the LDS-transpose kernels at head_dim
+    16 and 32 (unpack into head-major Q/K/V, merge into a head-major output,
+    split from a head-major O; 56 heads, the token count per rank scaled so
+    every op moves the representative shape's bytes), `reps` launches each,
+    for SQ counter runs."""
     import numpy as np
     import torch
 
@@ -964,20 +1093,32 @@ def run_pmc_sq(args):
         vrl.qkv_pack(*rk.qkv, rk.packed, w.P, w.C)
     torch.cuda.synchronize()
     del rk, hm
-    n16 = datagen.Workload(0, "16-element heads", P=w.P, C=w.C, s_local=w.s_local * w.D // 16, H=w.H, D=16,
-                           total_tokens=w.P * w.s_local * w.D // 16, seed=w.seed)
-    recv = torch.empty(3 * n16.s_local * n16.H * n16.D, dtype=torch.bfloat16, device=dev)
-    recv.view(torch.int16).random_(-30000, 30000)
-    hm = [torch.empty(n16.G, n16.S, n16.D, dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    for _ in range(args.reps):
-        vrl.qkv_unpack(recv, *[t.transpose(0, 1) for t in hm], n16.P, n16.C)
-    torch.cuda.synchronize()
-    print(f"pmc-sq: {args.reps} x head-run unpack (head-major), direct unpack, pack, "
-          f"LDS-transpose unpack (head-major, D=16)", flush=True)
+    for D in (16, 32):
+        n = datagen.Workload(0, f"{D}-element heads", P=w.P, C=w.C, s_local=w.s_local * w.D // D, H=w.H, D=D,
+                             total_tokens=w.P * w.s_local * w.D // D, seed=w.seed)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        recv = torch.empty(3 * n.s_local * n.H * D, **bf)
+        recv.view(torch.int16).random_(-30000, 30000)
+        hm = [torch.empty(n.G, n.S, D, **bf) for _ in range(3)]
+        out = torch.empty(n.H, n.s_local, D, **bf)
+        send = torch.empty(n.s_local * n.H * D, **bf)
+        for _ in range(args.reps):
+            vrl.qkv_unpack(recv, *[t.transpose(0, 1) for t in hm], n.P, n.C)
+        for _ in range(args.reps):
+            vrl.head_merge(recv[:send.numel()], out.transpose(0, 1), n.P, n.C)
+        for _ in range(args.reps):
+            vrl.attn_split(hm[0].transpose(0, 1), send, n.P, n.C)
+        torch.cuda.synchronize()
+        del recv, hm, out, send
+    print(f"pmc-sq: {args.reps} x head-run unpack (head-major), direct unpack, pack, and at head_dim 16 "
+          f"and 32 the LDS-transpose unpack, merge and split (head-major)", flush=True)
 
 
 def sq_summary(d):
-    """Mean per-dispatch value of every counter in a --pmc tree, per kernel."""
+    """Mean per-dispatch value of every counter in a --pmc tree, per kernel
+    and grid (labelled with the workload when the grid is one this benchmark
+    launches whole-tensor)."""
+    whole = whole_tensor_grids()
     rows = {}
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
@@ -985,13 +1126,16 @@ def sq_summary(d):
                 lab = kernel_label(r["Kernel_Name"])
                 if lab is None:
                     continue
-                rows.setdefault((lab[1] + " " + lab[0], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                grid = int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+                suffix = whole.get((lab[0], lab[1], grid), ("",))[0]
+                rows.setdefault((lab[1] + " " + lab[0] + suffix, r["Counter_Name"]), []).append(
+                    float(r["Counter_Value"]))
     kernels = sorted({k for k, _ in rows})
     counters = sorted({c for _, c in rows})
-    print(f"{'kernel':<22}" + "".join(f"{c:>24}" for c in counters))
+    print(f"{'kernel':<40}" + "".join(f"{c:>24}" for c in counters))
     for k in kernels:
         vals = [rows.get((k, c)) for c in counters]
-        print(f"{k:<22}" + "".join(f"{(sum(v) / len(v) if v else float('nan')):24.0f}" for v in vals))
+        print(f"{k:<40}" + "".join(f"{(sum(v) / len(v) if v else float('nan')):24.0f}" for v in vals))
 
 
 def pmc_summary(fetch_dir, write_dir):
@@ -1085,7 +1229,7 @@ def whole_tensor_grids():
         for op in ("qkv_unpack", "attn_split", "head_merge"):
             # a gather's tiles hold the whole group, a scatter's a line's worth of heads
             gt = G if op == "attn_split" else next(g for g in range(1, G + 1) if G % g == 0 and g * D * 2 >= 128)
-            tt = 16384 // ((gt * hv + 1) * 16)
+            tt = 16384 // (gt * hv * 16)
             tt = min(tt - tt % quantum, t_max)
             blocks = base.P * base.C * (3 if op == "qkv_unpack" else 1)
             nbytes = op_bytes(base)[op]
@@ -1093,6 +1237,45 @@ def whole_tensor_grids():
             label = f" (head_dim {D})" if key not in out else out[key][0][:-1] + f", {D})"
             out[key] = (label, nbytes)
     return out
+
+
+def windows_summary(d):
+    """Dispatch durations of the one-chunk window launches in a rocprofv3
+    --kernel-trace run of `bench.py --mode windows` (representative shape):
+    per op, all C windows together (same grid), with the rate on a window's
+    mean algorithmic bytes (the op's bytes / C)."""
+    import datagen
+
+    paths = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    w = datagen.WORKLOADS[3]
+    nb = op_bytes(w)
+    t_max = -(-w.s_local // w.C)
+    tiles = -(-t_max * (w.G * w.D // 8) // 2048)
+    grid_of = {op: 256 * w.P * (3 if op in ("qkv_pack", "qkv_unpack") else 1) * tiles for op in nb}
+    times = {}
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            lab = kernel_label(r["Kernel_Name"])
+            grid = int(r["Grid_Size_X"])
+            if lab is None or lab[1] != "direct" or grid_of[lab[0]] != grid:
+                continue
+            times.setdefault(lab[0], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"# kernel sources: sha256 prefix {kernel_source_hash()}")
+    print(f"# one-chunk windows [c, c+1), c = 0..{w.C - 1}, representative shape; bytes = the op's / {w.C}")
+    print(f"{'op':<12} {'grid':>9} {'calls':>5} {'median_us':>10} {'p10_us':>8} {'p90_us':>8} {'avg_us':>8}"
+          f" {'bytes':>11} {'GB/s(med)':>10} {'%8TB/s':>7}")
+    for op in nb:
+        ts = sorted(times.get(op, []))
+        if not ts:
+            continue
+        n = len(ts)
+        med = ts[n // 2]
+        nbytes = nb[op] // w.C
+        gbs = nbytes / (med * 1e-6) / 1e9
+        print(f"{op:<12} {grid_of[op]:>9} {n:>5} {med:10.1f} {ts[n // 10]:8.1f} {ts[(9 * n) // 10]:8.1f}"
+              f" {sum(ts) / n:8.1f} {nbytes:>11} {gbs:10.0f} {100 * gbs / PEAK_HBM_GBS:7.1f}")
 
 
 def trace_summary(d):
@@ -1139,6 +1322,9 @@ def main():
     if args.sq_summary:
         sq_summary(args.sq_summary)
         return
+    if args.windows_summary:
+        windows_summary(args.windows_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the P ranks' "
               f"buffers and their exchange are modelled inside one GPU's HBM; a multi-GPU run "
@@ -1146,6 +1332,8 @@ def main():
         sys.exit(2)
     if args.mode == "pmc":
         run_pmc(args)
+    elif args.mode == "windows":
+        run_windows(args)
     elif args.mode == "pmc-sq":
         run_pmc_sq(args)
     else:
