@@ -51,8 +51,13 @@
  *   VRL_E_INVALID  bad dimensions (P, C, S_l, H, D < 1; H % P != 0; C > S_l
  *                  for token chunks; G % C != 0 for head chunks),
  *                  a bad window, a null pointer, a size beyond the supported
- *                  range, or a view that extends past the end of its device
- *                  allocation.
+ *                  range, or a view that extends past the device allocation
+ *                  holding its base pointer.  The allocation is what the HIP
+ *                  runtime reports (hipMemGetAddressRange): a caching
+ *                  allocator's segment can hold several tensors, and a view
+ *                  that overruns its tensor but stays inside the segment is
+ *                  accepted and written.  Strides that fit the caller's
+ *                  tensors are the caller's responsibility.
  *   VRL_E_LAYOUT   an out-of-contract layout: a negative stride, an output
  *                  view whose elements overlap each other, overlapping output
  *                  views, an output that overlaps an input, or a pointer that

@@ -66,7 +66,7 @@ def test_view_past_allocation_rejected(gpu):
     try:
         base, size = ctypes.c_void_p(), ctypes.c_size_t()
         assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), region.value) == 0
-        assert base.value == region.value and size.value >= 1 << 20
+        assert base.value == region.value and size.value == 1 << 20
         P, C, S_l, H, D = 2, 2, 16, 4, 8
         G, S = H // P, P * S_l
         send = base.value
@@ -121,3 +121,63 @@ def test_rejected_calls_write_nothing(gpu):
     torch.cuda.synchronize()
     assert_guard_intact(whole, "valid call after rejections")
     say("rejections ok")
+
+
+def test_extent_check_is_per_allocation(gpu):
+    """The extent check compares each view with the device allocation that
+    holds it (as hipMemGetAddressRange reports it; under torch's caching
+    allocator that is a segment, which may hold several tensors), not with
+    the tensor the caller means.  An output view that runs past its tensor
+    into a neighbouring tensor of the same allocation is therefore accepted
+    and writes there; one that runs past the allocation's end is rejected
+    with VRL_E_INVALID and writes nothing."""
+    from tests.gpu_harness import SENTINEL
+
+    L = _lib.lib()
+    P, C, S_l, H, D = 2, 2, 8, 4, 8
+    n = S_l * H * D
+    recv = to_dev(np.arange(1, n + 1, dtype=np.uint16), gpu)
+
+    # inside one allocation: x and its neighbour are views of one tensor
+    arena = torch.full((3 * n,), SENTINEL, dtype=torch.int16, device=gpu)
+    x = arena[n:2 * n]
+    st = H * D + 1          # rows one element too far apart: the last row ends past x
+    assert L.vrl_head_merge(_d(P, C, S_l, H, D), recv.data_ptr(), _v(x.data_ptr(), st, D), 0, C, None) \
+        == _lib.VRL_OK, _lib.last_error()
+    torch.cuda.synchronize()
+    end = (S_l - 1) * st + H * D            # elements of the view's span, from x's start
+    assert end > n
+    assert bool((arena[2 * n:n + end] != SENTINEL).any()), "the over-reach did not reach the neighbour"
+    assert bool((arena[:n] == SENTINEL).all()) and bool((arena[n + end:] == SENTINEL).all())
+
+    # past the allocation: a hipMalloc'd region filled with 0xAB bytes
+    hip = _hip()
+    hip.hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipDeviceSynchronize.argtypes = []
+    region = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(region), 1 << 20) == 0
+    try:
+        base, size = ctypes.c_void_p(), ctypes.c_size_t()
+        assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), region.value) == 0
+        # the runtime's range is exactly this allocation (else the views below
+        # would be placed relative to memory this test does not own)
+        assert base.value == region.value and size.value == 1 << 20
+        assert hip.hipMemset(region.value, 0xAB, size.value) == 0
+        assert hip.hipDeviceSynchronize() == 0
+        out = base.value + size.value - 2 * n + 2 * H * D        # the last row one row past the end
+        assert L.vrl_head_merge(_d(P, C, S_l, H, D), recv.data_ptr(), _v(out, H * D, D), 0, C, None) \
+            == _lib.VRL_E_INVALID
+        assert "past its allocation" in _lib.last_error()
+        assert hip.hipDeviceSynchronize() == 0
+        host = np.empty(size.value, np.uint8)
+        assert hip.hipMemcpy(host.ctypes.data, base.value, size.value, 2) == 0   # device to host
+        assert bool((host == 0xAB).all()), "a rejected call wrote into the allocation"
+        # one row earlier the view fits and the call runs
+        assert L.vrl_head_merge(_d(P, C, S_l, H, D), recv.data_ptr(), _v(out - 2 * H * D, H * D, D), 0, C,
+                                None) == _lib.VRL_OK, _lib.last_error()
+        assert hip.hipDeviceSynchronize() == 0
+    finally:
+        torch.cuda.synchronize()
+        hip.hipFree(region.value)
+    say("extent check per allocation ok")
