@@ -1218,6 +1218,10 @@ def whole_tensor_grids():
             out[(op, "direct", direct)] = (suffix, nbytes)
             out[(op, "direct strided-heads", direct)] = (suffix, nbytes)
             out[(op, "head-run", 256 * blocks * w.G * -(-t_max // tt))] = (suffix, nbytes)
+    # the copy ceiling: a pack with P = 1, C = 1 of the representative shape
+    w = datagen.WORKLOADS[3]
+    out[("qkv_pack", "direct", 256 * 3 * -(-w.s_local * w.H * w.D // 8 // 2048))] = (
+        " (copy ceiling: P=1, C=1)", op_bytes(w)["qkv_pack"])
     # the narrow-head workloads (LDS transpose: tiles of Gt heads filling a
     # 128-byte line x as many tokens as fit 16 KiB, rounded to whole lines)
     base = datagen.WORKLOADS[3]
