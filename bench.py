@@ -15,16 +15,21 @@ they run once before timing to fill the receive buffers and are not timed.
 Printed: one JSON line with the whole step's effective HBM throughput
 (algorithmic bytes: every element read once and written once), per-op
 times from HIP events recorded on the launch stream, the roofline of the
-dominant kernel (QKV pack) against the 8 TB/s HBM3E peak, a device-to-device
-copy of the pack's size for comparison, sections for the other layouts and
-workloads (untimed by the step), and the CPU oracle timed on the host's
-cores over one step of the workload (median of five passes).
+dominant kernel (QKV pack) against the 8 TB/s HBM3E peak, copies of the
+same bytes for comparison (the runtime's device-to-device copy, torch's
+elementwise kernel, and the library's own copy core on a plain contiguous
+relayout), sections outside the timed step (one-chunk windows, the overlap
+schedule with each stand-in exchange, the other layouts and workloads, the
+reference chains), and the CPU oracle timed on the host's cores over one
+step of the workload.
 
-Other modes: --mode pmc launches each relayout kernel the representative
-shape uses, token-major and head-major layouts (rank 0), and a plain torch
-copy kernel of known size, for rocprofv3 counter runs; --pmc-summary turns
-the counter CSVs of those runs into the traffic figures kept under
-profiles/.
+Other modes: --mode windows runs only the one-chunk windows (for a kernel
+trace of their own); --mode pmc launches each relayout kernel the
+representative shape uses, token-major and head-major layouts (rank 0), and
+a plain torch copy kernel of known size, for rocprofv3 counter runs;
+--mode pmc-sq the kernels of the SQ/TCC counter runs; --pmc-summary,
+--sq-summary, --trace-summary and --windows-summary turn the CSVs of such
+runs into the summaries kept under profiles/.
 """
 from __future__ import annotations
 
