@@ -826,22 +826,33 @@ def strided_rows(torch, np, datagen, vrl, dev):
     return out
 
 
-def smaller_workloads(torch, np, datagen, vrl, dev, wids=(2, 5), reps=12):
+def shard_workloads(datagen):
+    """One rank's share of the representative 55,413-token sequence over 4
+    and 8 ranks (55,416 tokens after padding; 56 heads of 128, four token
+    chunks): the shapes each GPU of a four- or eight-GPU run would relayout."""
+    base = datagen.WORKLOADS[3]
+    return [datagen.Workload(0, f"representative sequence over P={P}", P=P, C=base.C,
+                             s_local=-(-base.total_tokens // P), H=base.H, D=base.D,
+                             total_tokens=base.total_tokens, seed=base.seed) for P in (4, 8)]
+
+
+def smaller_workloads(torch, np, datagen, vrl, dev, reps=12):
     """The four relayouts at the mid-size (P=2, 4,096 tokens/rank, 32 heads)
-    and P=4 (7,752 tokens/rank, 32 heads) workloads, rank 0's share.  Their
-    working sets fit the 256 MB Infinity Cache, so each op rotates over k
-    copies of its buffers with k x bytes per launch >= 1 GiB: every launch
-    reads inputs that the previous launches have evicted."""
+    and P=4 (7,752 tokens/rank, 32 heads) workloads and at one rank's share
+    of the representative sequence over 4 and 8 ranks (13,854 and 6,927
+    tokens per rank, 56 heads), rank 0's share.  Each op rotates over k
+    copies of its buffers with k x bytes per launch >= 1 GiB, so every launch
+    reads inputs that the previous launches have evicted from the 256 MB
+    Infinity Cache; per-call HIP events and the queue's mean per call."""
     out = {}
-    for wid in wids:
-        w = datagen.WORKLOADS[wid]
+    for w in [datagen.WORKLOADS[2], datagen.WORKLOADS[5]] + shard_workloads(datagen):
         P, C, S_l, H, D, G, S = w.P, w.C, w.s_local, w.H, w.D, w.G, w.S
         nb = op_bytes(w)
         bf = dict(dtype=torch.bfloat16, device=dev)
         host = datagen.fused_source(w, 0)
         fused0 = torch.from_numpy(host.view(np.int16)).to(dev).view(torch.bfloat16)
-        k_big = -(-(1 << 30) // nb["qkv_pack"])
-        k_small = -(-(1 << 30) // nb["head_merge"])
+        k_big = _sets_for(nb["qkv_pack"], 64)
+        k_small = _sets_for(nb["head_merge"], 64)
         sets = []
         for i in range(max(k_big, k_small)):
             fused = fused0.clone()
@@ -863,27 +874,18 @@ def smaller_workloads(torch, np, datagen, vrl, dev, wids=(2, 5), reps=12):
         for name, (k, fn) in ops.items():
             for i in range(k):
                 fn(sets[i])
-            pairs = []
-            for i in range(reps * k):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn(sets[i % k])
-                e1.record()
-                pairs.append((e0, e1))
-            torch.cuda.synchronize()
-            ts = sorted(a.elapsed_time(b) for a, b in pairs)
-            ms = ts[len(ts) // 2]
-            gbs = nb[name] / (ms * 1e-3) / 1e9
-            res[name] = {"ms": round(ms, 5), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
-                         "buffer_sets": k, "launches": len(ts)}
-        # the rotation must not have changed what the ops compute
+            ts, mean = _queued(torch, fn, sets[:k], reps * k)
+            res[name] = _stats(ts, mean, nb[name])
+            res[name]["buffer_sets"] = k
+        # the rotation must not have changed what the ops compute; the merge of
+        # the split of the unpack of a rank's own packed buffer returns its Q
         ref = sets[0]
         for st in sets[1:]:
             if not (torch.equal(st["packed"].view(torch.int16), ref["packed"].view(torch.int16))
                     and torch.equal(st["merged"].view(torch.int16), ref["merged"].view(torch.int16))):
-                raise SystemExit(f"workload {wid}: buffer sets disagree")
+                raise SystemExit(f"{w.name}: buffer sets disagree")
         if not torch.equal(ref["merged"].view(torch.int16), ref["qkv"][0].view(torch.int16)):
-            raise SystemExit(f"workload {wid}: round trip is not bit-exact")
+            raise SystemExit(f"{w.name}: round trip is not bit-exact")
         out[w.name] = res
         del sets
     return out
@@ -1210,8 +1212,9 @@ def whole_tensor_grids():
     import datagen
 
     out = {}
-    for wid, suffix in ((3, ""), (2, " (mid-size)"), (5, " (P=4)")):
-        w = datagen.WORKLOADS[wid]
+    shards = shard_workloads(datagen)
+    for w, suffix in ((datagen.WORKLOADS[3], ""), (datagen.WORKLOADS[2], " (mid-size)"),
+                      (datagen.WORKLOADS[5], " (P=4)"), (shards[0], " (P=4 shard)"), (shards[1], " (P=8 shard)")):
         nb = op_bytes(w)
         t_max = -(-w.s_local // w.C)
         head_vecs = w.D // 8

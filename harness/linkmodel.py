@@ -45,6 +45,8 @@ def exchange(pairs, link_gbs: float = XGMI_LINK_GBS) -> None:
         return
     blocks = (Block * len(pairs))()
     for i, (src, dst, paced) in enumerate(pairs):
+        if not (src.is_cuda and dst.is_cuda and src.device == dst.device):
+            raise ValueError("exchange blocks must be device tensors of one device")
         if src.numel() != dst.numel() or src.dtype != dst.dtype or not (src.is_contiguous() and dst.is_contiguous()):
             raise ValueError("exchange blocks must be dense and of equal size")
         blocks[i] = Block(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(), int(bool(paced)))
