@@ -24,7 +24,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr int kMaxBlocks = 64;
-constexpr uint32_t kGroupsPerBlock = 32;  // workgroups sharing one block
+// Workgroups sharing one block: one per kGbsPerGroup of link rate, within
+// [kMinGroups, kMaxGroups].  A workgroup keeps one 32 KiB piece in flight
+// and copies about 7 GB/s on its own, so each paced one is asked for less
+// than half of that.
+constexpr double kGbsPerGroup = 3.0;
+constexpr uint32_t kMinGroups = 8, kMaxGroups = 128;
 
 struct Block {
     const void *src;
@@ -122,8 +127,9 @@ typedef struct {
 } lm_block;
 
 // Enqueues one exchange of `n` blocks (1 <= n <= 64) on `stream` (a
-// hipStream_t, NULL for the default stream): one kernel, 32 workgroups per
-// block, paced blocks at `link_gbs` 1e9 B/s each (1 <= link_gbs <= 10000).
+// hipStream_t, NULL for the default stream): one kernel, 8 to 128
+// workgroups per block (one per 3 GB/s of link rate), paced blocks at
+// `link_gbs` 1e9 B/s each (1 <= link_gbs <= 10000).
 // Returns 0, or 1 with a message from lm_last_error() and nothing enqueued.
 __attribute__((visibility("default"))) int lm_exchange(const lm_block *blocks, int32_t n, double link_gbs,
                                                        void *stream)
@@ -159,15 +165,17 @@ __attribute__((visibility("default"))) int lm_exchange(const lm_block *blocks, i
         return fail("a paced block would take longer than one second");
     const int vb = narrow ? 2 : 16;
     const double piece_bytes = double(kThreads) * kUnroll * vb;
+    uint32_t groups = uint32_t(link_gbs / kGbsPerGroup + 0.999);
+    groups = groups < kMinGroups ? kMinGroups : groups > kMaxGroups ? kMaxGroups : groups;
     a.nblocks = n;
-    a.groups = kGroupsPerBlock;
-    a.ticks_per_piece = uint64_t(piece_bytes * kGroupsPerBlock / (link_gbs * 1e9) * khz * 1e3);
+    a.groups = groups;
+    a.ticks_per_piece = uint64_t(piece_bytes * groups / (link_gbs * 1e9) * khz * 1e3);
     // a sleep lasts at least about 50 ns; allow ten times the paced time's worth
     a.max_spins = uint64_t(secs * 1e9 / 5.0) + 100000;
     void *kargs[] = {&a};
     const void *fn = narrow ? reinterpret_cast<const void *>(&paced_copy<2>)
                             : reinterpret_cast<const void *>(&paced_copy<16>);
-    const hipError_t e = hipLaunchKernel(fn, dim3(uint32_t(n) * kGroupsPerBlock), dim3(kThreads), kargs, 0,
+    const hipError_t e = hipLaunchKernel(fn, dim3(uint32_t(n) * groups), dim3(kThreads), kargs, 0,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(hipGetErrorString(e));
