@@ -1203,12 +1203,20 @@ def pmc_summary(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+# The launch planner's workgroup shapes (head_relayout_amd/csrc/vrl_internal.h),
+# for labelling trace rows by grid size: lanes per workgroup and vectors per
+# tile of the direct and head-run kernels, lanes of the LDS transpose.
+DIRECT_THREADS, DIRECT_TILE = 64, 64
+HEADRUN_THREADS, HEADRUN_TILE = 128, 256
+STAGED_THREADS = 256
+
+
 def whole_tensor_grids():
     """{(op, kind, grid in threads): (workload suffix, algorithmic bytes)} for
     the whole-tensor launches of the workloads this benchmark runs.  It
-    follows the launch planner's tiling at 16-byte vectors: 256-lane
-    workgroups, 2,048 vectors per direct tile, head-run tiles of as many
-    tokens of one head as fill 2,048 vectors."""
+    follows the launch planner's tiling at 16-byte vectors: one-wave direct
+    workgroups of 64 vectors, head-run workgroups of as many tokens of one
+    head as fill 256 vectors."""
     import datagen
 
     out = {}
@@ -1219,16 +1227,16 @@ def whole_tensor_grids():
         t_max = -(-w.s_local // w.C)
         head_vecs = w.D // 8
         row_vecs = w.G * head_vecs
-        tt = min(2048 // head_vecs, t_max)
+        tt = min(HEADRUN_TILE // head_vecs, t_max)
         for op, nbytes in nb.items():
             blocks = w.P * w.C * (3 if op in ("qkv_pack", "qkv_unpack") else 1)
-            direct = 256 * blocks * -(-t_max * row_vecs // 2048)
+            direct = DIRECT_THREADS * blocks * -(-t_max * row_vecs // DIRECT_TILE)
             out[(op, "direct", direct)] = (suffix, nbytes)
             out[(op, "direct strided-heads", direct)] = (suffix, nbytes)
-            out[(op, "head-run", 256 * blocks * w.G * -(-t_max // tt))] = (suffix, nbytes)
+            out[(op, "head-run", HEADRUN_THREADS * blocks * w.G * -(-t_max // tt))] = (suffix, nbytes)
     # the copy ceiling: a pack with P = 1, C = 1 of the representative shape
     w = datagen.WORKLOADS[3]
-    out[("qkv_pack", "direct", 256 * 3 * -(-w.s_local * w.H * w.D // 8 // 2048))] = (
+    out[("qkv_pack", "direct", DIRECT_THREADS * 3 * -(-w.s_local * w.H * w.D // 8 // DIRECT_TILE))] = (
         " (copy ceiling: P=1, C=1)", op_bytes(w)["qkv_pack"])
     # the narrow-head workloads (LDS transpose: tiles of Gt heads filling a
     # 128-byte line x as many tokens as fit 16 KiB, rounded to whole lines)
@@ -1245,7 +1253,7 @@ def whole_tensor_grids():
             tt = min(tt - tt % quantum, t_max)
             blocks = base.P * base.C * (3 if op == "qkv_unpack" else 1)
             nbytes = op_bytes(base)[op]
-            key = (op, "staged", 256 * blocks * (G // gt) * -(-t_max // tt))
+            key = (op, "staged", STAGED_THREADS * blocks * (G // gt) * -(-t_max // tt))
             label = f" (head_dim {D})" if key not in out else out[key][0][:-1] + f", {D})"
             out[key] = (label, nbytes)
     return out
@@ -1264,8 +1272,8 @@ def windows_summary(d):
     w = datagen.WORKLOADS[3]
     nb = op_bytes(w)
     t_max = -(-w.s_local // w.C)
-    tiles = -(-t_max * (w.G * w.D // 8) // 2048)
-    grid_of = {op: 256 * w.P * (3 if op in ("qkv_pack", "qkv_unpack") else 1) * tiles for op in nb}
+    tiles = -(-t_max * (w.G * w.D // 8) // DIRECT_TILE)
+    grid_of = {op: DIRECT_THREADS * w.P * (3 if op in ("qkv_pack", "qkv_unpack") else 1) * tiles for op in nb}
     times = {}
     with open(paths[0]) as f:
         for r in csv.DictReader(f):

@@ -8,12 +8,25 @@
 
 namespace vrl {
 
-// Workgroup shape.  A workgroup moves one tile of kThreads * kUnroll vectors
-// of one wire block; each lane issues kUnroll independent loads before its
-// stores.
-constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
-constexpr uint32_t kTileVecs = uint32_t(kThreads) * uint32_t(kUnroll);
+// Workgroup shapes.  The direct and head-run kernels move one tile per
+// workgroup, each lane issuing its loads before its stores; the staged
+// kernel moves its LDS tile in batches of kStagedBatch vectors.  The direct
+// kernel runs one wave per workgroup with one vector per lane: 1 KiB tiles,
+// dispatched in address order, each workgroup's slot refilled as soon as its
+// one wave is done.  The head-run kernel takes 128 lanes with two vectors
+// each (16 tokens of a 128-element head per tile); the LDS transpose needs
+// its 256 lanes to fill and drain a tile.
+constexpr int kDirectThreads = 64;
+constexpr int kDirectUnroll = 1;
+constexpr uint32_t kDirectTile = uint32_t(kDirectThreads) * uint32_t(kDirectUnroll);
+constexpr int kHeadrunThreads = 128;
+constexpr int kHeadrunUnroll = 2;
+constexpr uint32_t kHeadrunTile = uint32_t(kHeadrunThreads) * uint32_t(kHeadrunUnroll);
+constexpr int kStagedThreads = 256;
+constexpr int kStagedUnroll = 8;
+constexpr uint32_t kStagedBatch = uint32_t(kStagedThreads) * uint32_t(kStagedUnroll);
+// Bound on any tile or batch, for the planner's index-range checks.
+constexpr uint32_t kMaxTileVecs = kStagedBatch;
 
 // Head-major views (a head's tokens closer together than a token's heads)
 // whose head rows (2*D bytes) are narrower than this go through the LDS

@@ -18,16 +18,17 @@
 // unsigned vectors and never through float registers, so -0, subnormals and
 // NaN payloads are preserved.
 //
-// Mapping to CDNA4.  One workgroup (256 lanes, four wave64s) moves one tile
-// of kTileVecs consecutive vectors of one wire block; the grid is flattened
-// over (rank, chunk, plane, token tile).  Lanes take consecutive 16-byte
-// vectors, so a wave64 moves 1 KiB per instruction: four 128-element head
-// rows, contiguous on the wire side and, for head-contiguous views, on the
-// view side as well.  Each lane first issues all of its kUnroll loads and
-// only then its stores, which keeps 32 KiB per workgroup in flight.  The
-// dense wire offset of vector f is f itself; the view offset needs f's row
-// and column, obtained with a precomputed multiply-shift division.  Address
-// arithmetic is 64-bit wherever a product can pass 2^31 elements.
+// Mapping to CDNA4.  One workgroup of the direct kernel -- a single wave64
+// -- moves one tile of kDirectTile consecutive vectors of one wire block;
+// the grid is flattened over (rank, chunk, plane, token tile).  Lanes take
+// consecutive 16-byte vectors, so the wave moves 1 KiB per instruction: four
+// 128-element head rows, contiguous on the wire side and, for
+// head-contiguous views, on the view side as well.  Tiles this small keep
+// the chip's in-flight window in address order at fine grain: each wave's
+// slot is refilled with the next tile as soon as it is done.  The dense wire
+// offset of vector f is f itself; the view offset needs f's row and column,
+// obtained with a precomputed multiply-shift division.  Address arithmetic
+// is 64-bit wherever a product can pass 2^31 elements.
 //
 // Views stored head-major, written by a scatter, go through headrun_kernel
 // instead (each workgroup moves a run of one head's consecutive tokens), or,
@@ -216,11 +217,11 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
     return b;
 }
 
-// Direct kernel: each workgroup moves kTileVecs consecutive vectors of a
+// Direct kernel: each workgroup moves kDirectTile consecutive vectors of a
 // wire block; the view side follows.  Used for every call except scatters
 // into head-major views.
 template <Op OP, int VB, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
+__global__ __launch_bounds__(kDirectThreads) void relayout_kernel(const KernelArgs a)
 {
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
 
     const Block b = locate<OP>(a);
     const uint32_t nvec = uint32_t(b.T) * a.row_vecs;
-    const uint32_t f0 = b.tile * kTileVecs;
+    const uint32_t f0 = b.tile * kDirectTile;
     if (f0 >= nvec)
         return;
     const int64_t st = b.st, sh = b.sh;
@@ -255,19 +256,19 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(const KernelArgs a)
     };
 
     const uint32_t f_lane = f0 + threadIdx.x;
-    if (f0 + kTileVecs <= nvec) {
+    if (f0 + kDirectTile <= nvec) {
         // Full tile: all loads in flight before the first store.
-        V buf[kUnroll];
+        V buf[kDirectUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            buf[u] = load_vec(src_of(f_lane + uint32_t(u * kThreads)));
+        for (int u = 0; u < kDirectUnroll; ++u)
+            buf[u] = load_vec(src_of(f_lane + uint32_t(u * kDirectThreads)));
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            store_vec(dst_of(f_lane + uint32_t(u * kThreads)), buf[u]);
+        for (int u = 0; u < kDirectUnroll; ++u)
+            store_vec(dst_of(f_lane + uint32_t(u * kDirectThreads)), buf[u]);
     } else {
         // Last, partial tile of a block.
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t f = f_lane + uint32_t(u * kThreads);
+        for (int u = 0; u < kDirectUnroll; ++u) {
+            const uint32_t f = f_lane + uint32_t(u * kDirectThreads);
             if (f < nvec)
                 store_vec(dst_of(f), load_vec(src_of(f)));
         }
@@ -339,7 +340,7 @@ __device__ __forceinline__ void decode_run(const KernelArgs &a, uint32_t rest, u
 // different banks, while the wire-order phase, which walks along rows,
 // still sees a permutation of whole aligned groups of columns.
 template <Op OP, int VB>
-__global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
+__global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs a)
 {
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
@@ -392,13 +393,13 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
     };
 
     // Phase 1: source -> LDS, in the source's contiguous order.
-    for (uint32_t i0 = 0; i0 < nv; i0 += kTileVecs) {
-        V buf[kUnroll];
-        uint32_t slot[kUnroll];
-        bool ok[kUnroll];
+    for (uint32_t i0 = 0; i0 < nv; i0 += kStagedBatch) {
+        V buf[kStagedUnroll];
+        uint32_t slot[kStagedUnroll];
+        bool ok[kStagedUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
+        for (int u = 0; u < kStagedUnroll; ++u) {
+            const uint32_t i = i0 + uint32_t(u * kStagedThreads) + threadIdx.x;
             const Pos q = Tr::gather ? view_order(i < nv ? i : 0) : wire_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
             slot[u] = q.lds;
@@ -406,20 +407,20 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
                 buf[u] = load_vec(reinterpret_cast<const V *>((Tr::gather ? view : wire) + q.off));
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kStagedUnroll; ++u)
             if (ok[u])
                 lds[slot[u]] = buf[u];
     }
     __syncthreads();
     // Phase 2: LDS -> destination, in the destination's contiguous order (all
     // LDS reads of a batch first, then the stores).
-    for (uint32_t i0 = 0; i0 < nv; i0 += kTileVecs) {
-        V buf[kUnroll];
-        int64_t doff[kUnroll];
-        bool ok[kUnroll];
+    for (uint32_t i0 = 0; i0 < nv; i0 += kStagedBatch) {
+        V buf[kStagedUnroll];
+        int64_t doff[kStagedUnroll];
+        bool ok[kStagedUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i = i0 + uint32_t(u * kThreads) + threadIdx.x;
+        for (int u = 0; u < kStagedUnroll; ++u) {
+            const uint32_t i = i0 + uint32_t(u * kStagedThreads) + threadIdx.x;
             const Pos q = Tr::gather ? wire_order(i < nv ? i : 0) : view_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
             doff[u] = q.off;
@@ -427,20 +428,20 @@ __global__ __launch_bounds__(kThreads) void staged_kernel(const KernelArgs a)
                 buf[u] = lds[q.lds];
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kStagedUnroll; ++u)
             if (ok[u])
                 store_vec(reinterpret_cast<V *>((Tr::gather ? wire : view) + doff[u]), buf[u]);
     }
 }
 
 // Head-run kernel, for views stored head-major: a workgroup moves TT
-// consecutive tokens of one head of a wire block (TT * head_vecs <= kTileVecs
+// consecutive tokens of one head of a wire block (TT * head_vecs <= kHeadrunTile
 // vectors), and consecutive workgroups take consecutive token tiles of the
 // same head.  The head-major side then sees one contiguous run per
 // workgroup and the chip writes (or reads) few runs at a time; the wire side
 // sees TT pieces of D elements, one per wire row.
 template <Op OP, int VB>
-__global__ __launch_bounds__(kThreads) void headrun_kernel(const KernelArgs a)
+__global__ __launch_bounds__(kHeadrunThreads) void headrun_kernel(const KernelArgs a)
 {
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
@@ -474,17 +475,17 @@ __global__ __launch_bounds__(kThreads) void headrun_kernel(const KernelArgs a)
         return reinterpret_cast<V *>(Tr::gather ? wire + off(i, row) : view + off(i, st));
     };
 
-    if (nv == kTileVecs) {
-        V buf[kUnroll];
+    if (nv == kHeadrunTile) {
+        V buf[kHeadrunUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            buf[u] = load_vec(src_of(threadIdx.x + uint32_t(u * kThreads)));
+        for (int u = 0; u < kHeadrunUnroll; ++u)
+            buf[u] = load_vec(src_of(threadIdx.x + uint32_t(u * kHeadrunThreads)));
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            store_vec(dst_of(threadIdx.x + uint32_t(u * kThreads)), buf[u]);
+        for (int u = 0; u < kHeadrunUnroll; ++u)
+            store_vec(dst_of(threadIdx.x + uint32_t(u * kHeadrunThreads)), buf[u]);
     } else {
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i = threadIdx.x + uint32_t(u * kThreads);
+        for (int u = 0; u < kHeadrunUnroll; ++u) {
+            const uint32_t i = threadIdx.x + uint32_t(u * kHeadrunThreads);
             if (i < nv)
                 store_vec(dst_of(i), load_vec(src_of(i)));
         }
@@ -498,13 +499,13 @@ hipError_t launch_vb(const LaunchPlan &pl, hipStream_t stream)
     void *kargs[] = {&args};
     if (pl.headrun)
         return hipLaunchKernel(reinterpret_cast<const void *>(&headrun_kernel<OP, VB>), dim3(pl.grid),
-                               dim3(kThreads), kargs, 0, stream);
+                               dim3(kHeadrunThreads), kargs, 0, stream);
     if (pl.lds_bytes)
         return hipLaunchKernel(reinterpret_cast<const void *>(&staged_kernel<OP, VB>), dim3(pl.grid),
-                               dim3(kThreads), kargs, pl.lds_bytes, stream);
+                               dim3(kStagedThreads), kargs, pl.lds_bytes, stream);
     const void *fn = pl.contig ? reinterpret_cast<const void *>(&relayout_kernel<OP, VB, true>)
                                : reinterpret_cast<const void *>(&relayout_kernel<OP, VB, false>);
-    return hipLaunchKernel(fn, dim3(pl.grid), dim3(kThreads), kargs, 0, stream);
+    return hipLaunchKernel(fn, dim3(pl.grid), dim3(kDirectThreads), kargs, 0, stream);
 }
 
 template <Op OP>

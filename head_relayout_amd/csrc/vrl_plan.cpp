@@ -85,7 +85,7 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     const int64_t row_vecs = Gb * d->D / ve;
     const int64_t t_max = d->chunk_heads ? d->s_local : chunk_q + (chunk_r ? 1 : 0);
     if (t_max > (int64_t(1) << 31) / row_vecs ||
-        t_max * row_vecs + int64_t(kTileVecs) >= (int64_t(1) << 31)) {
+        t_max * row_vecs + int64_t(kMaxTileVecs) >= (int64_t(1) << 31)) {
         *why = "a chunk is too large (2^31 vectors or more); use more chunks";
         return false;
     }
@@ -98,14 +98,14 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     a.head_vecs = uint32_t(d->D / ve);
     magic_for(a.row_vecs, a.row_magic, a.row_shift);
     magic_for(a.head_vecs, a.head_magic, a.head_shift);
-    a.tiles = uint32_t((nvec_max + kTileVecs - 1) / kTileVecs);
+    a.tiles = uint32_t((nvec_max + kDirectTile - 1) / kDirectTile);
 
     // A view whose heads lie further apart than its tokens (head-major
     // storage) makes the token and head axes swap for real: in wire order a
     // workgroup's writes into it scatter 2*D-byte pieces over all Gb heads,
     // and the chip has every head's stream open at once.  Scatters into such
     // views run as head runs instead: a workgroup moves TT consecutive
-    // tokens of one head (TT * head_vecs <= kTileVecs), consecutive
+    // tokens of one head (TT * head_vecs <= kHeadrunTile), consecutive
     // workgroups continue the same head.  Head rows narrower than a cache
     // line would make those runs read partial lines on the wire side, and
     // make wire-order gathers read partial lines of the view; such views go
@@ -152,8 +152,8 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
             ++a.swz_shift;
         pl.lds_bytes = uint32_t(tt * lrow_bytes);
         tiles = (Gb / gt) * int64_t(a.tok_tiles);
-    } else if (!gather && a.head_vecs <= kTileVecs) {
-        const int64_t tt = std::min<int64_t>(kTileVecs / a.head_vecs, t_max);
+    } else if (!gather && a.head_vecs <= kHeadrunTile) {
+        const int64_t tt = std::min<int64_t>(kHeadrunTile / a.head_vecs, t_max);
         pl.headrun = true;
         a.tile_tokens = uint32_t(tt);
         a.tok_tiles = uint32_t((t_max + tt - 1) / tt);

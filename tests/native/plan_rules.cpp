@@ -7,7 +7,7 @@
 // head rows narrower than a 128-byte line take the LDS transpose (for a
 // scatter Gt heads filling a line, for a gather the whole group, x as many
 // tokens as fit 16 KiB);
-// scatters into head-major views with wider rows take head runs (128 tokens
+// scatters into head-major views with wider rows take head runs (16 tokens
 // of one head per workgroup at head_dim 128), gathers from them the direct
 // kernel; so does any view whose head row is longer than one tile or whose
 // group has one head.
@@ -94,17 +94,18 @@ int main()
     // representative shape: P=2, C=4, 27,707 tokens per rank, 56 heads of 128
     const int64_t R = 27707;
     const Case cases[] = {
-        {"pack, fused token-major source", Op::Pack, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 36384, 16},
-        {"unpack, token-major", Op::Unpack, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 36384, 16},
-        {"split, token-major", Op::Split, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 12128, 16},
-        {"merge, token-major", Op::Merge, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 12128, 16},
-        // 28 heads x 55 token tiles of 128 per (rank, chunk, plane)
-        {"unpack into head-major, D=128", Op::Unpack, 2, 4, R, 56, 128, 0, true, 0, HEADRUN, 128, 0, 36960, 16},
-        {"merge into head-major, D=128", Op::Merge, 2, 4, R, 56, 128, 0, true, 0, HEADRUN, 128, 0, 12320, 16},
-        {"split from head-major, D=128", Op::Split, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 12128, 16},
-        {"pack from head-major, D=128", Op::Pack, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 36384, 16},
-        {"unpack into head-major, head chunks", Op::Unpack, 2, 4, R, 56, 128, 1, true, 0, HEADRUN, 128, 0, 0, 16},
-        {"unpack into head-major, D=64", Op::Unpack, 2, 4, 2 * R, 56, 64, 0, true, 0, HEADRUN, 256, 0, 0, 16},
+        // 1 KiB direct tiles: 6,927 tokens x 448 vectors / 64 = 48,489 per (rank, chunk, plane)
+        {"pack, fused token-major source", Op::Pack, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 1163736, 16},
+        {"unpack, token-major", Op::Unpack, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 1163736, 16},
+        {"split, token-major", Op::Split, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 387912, 16},
+        {"merge, token-major", Op::Merge, 2, 4, R, 56, 128, 0, false, 0, DIRECT, 0, 0, 387912, 16},
+        // 28 heads x 433 token tiles of 16 per (rank, chunk, plane)
+        {"unpack into head-major, D=128", Op::Unpack, 2, 4, R, 56, 128, 0, true, 0, HEADRUN, 16, 0, 290976, 16},
+        {"merge into head-major, D=128", Op::Merge, 2, 4, R, 56, 128, 0, true, 0, HEADRUN, 16, 0, 96992, 16},
+        {"split from head-major, D=128", Op::Split, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 387912, 16},
+        {"pack from head-major, D=128", Op::Pack, 2, 4, R, 56, 128, 0, true, 0, DIRECT, 0, 0, 1163736, 16},
+        {"unpack into head-major, head chunks", Op::Unpack, 2, 4, R, 56, 128, 1, true, 0, HEADRUN, 16, 0, 0, 16},
+        {"unpack into head-major, D=64", Op::Unpack, 2, 4, 2 * R, 56, 64, 0, true, 0, HEADRUN, 32, 0, 0, 16},
         // 126-byte head rows: 2 heads fill a line; 2*63 2-byte vectors per LDS row
         {"unpack into head-major, D=63", Op::Unpack, 2, 3, 20, 4, 63, 0, true, 0, STAGED, 7, 2, 0, 2},
         // 4 heads x 32 B fill a line; 8 vectors per LDS row -> 128 tokens

@@ -89,9 +89,10 @@ def test_trace_summary_labels_workloads_and_windows(tmp_path, capsys):
     import bench
 
     pack = "void vrl::(anonymous namespace)::relayout_kernel<(vrl::Op)0, 16, true>(vrl::KernelArgs)"
-    rows = [(pack, 9314304, 400_000), (pack, 9314304, 400_000),   # representative: 400 us
-            (pack, 1499136, 66_000),                               # P=4 whole tensor
-            (pack, 2328576, 100_000),                              # one chunk of the representative
+    # grids in work-items: one-wave workgroups of 64 vectors (1 KiB) each
+    rows = [(pack, 74479104, 400_000), (pack, 74479104, 400_000),  # representative: 400 us
+            (pack, 11907072, 66_000),                              # P=4 whole tensor
+            (pack, 18619776, 100_000),                             # one chunk of the representative
             ("__amd_rocclr_copyBuffer", 131072, 50_000)]
     d = tmp_path / "trace"
     d.mkdir()
@@ -101,7 +102,7 @@ def test_trace_summary_labels_workloads_and_windows(tmp_path, capsys):
             f.write(f'"{name}",{grid},1000,{1000 + ns}\n')
     bench.trace_summary(str(d))
     out = capsys.readouterr().out.splitlines()
-    rep = [l for l in out if l.startswith("direct qkv_pack ") and " 9314304 " in l]
+    rep = [l for l in out if l.startswith("direct qkv_pack ") and " 74479104 " in l]
     assert len(rep) == 1 and rep[0].split()[-2:] == ["5958", "74.5"], rep   # 2,383,245,312 B / 400 us
     p4 = [l for l in out if l.startswith("direct qkv_pack (P=4)")]
     assert len(p4) == 1 and p4[0].split()[-2:] == ["5773", "72.2"], p4     # 381,026,304 B / 66 us
