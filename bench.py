@@ -1234,6 +1234,13 @@ def whole_tensor_grids():
             out[(op, "direct", direct)] = (suffix, nbytes)
             out[(op, "direct strided-heads", direct)] = (suffix, nbytes)
             out[(op, "head-run", HEADRUN_THREADS * blocks * w.G * -(-t_max // tt))] = (suffix, nbytes)
+    # the representative shape with head chunks (rows of G / C heads, all S_l tokens)
+    w = datagen.WORKLOADS[3]
+    nb = op_bytes(w)
+    hc_rows = -(-w.s_local * (w.G // w.C) * (w.D // 8) // DIRECT_TILE)
+    for op, nbytes in nb.items():
+        blocks = w.P * w.C * (3 if op in ("qkv_pack", "qkv_unpack") else 1)
+        out.setdefault((op, "direct", DIRECT_THREADS * blocks * hc_rows), (" (head chunks)", nbytes))
     # the copy ceiling: a pack with P = 1, C = 1 of the representative shape
     w = datagen.WORKLOADS[3]
     out[("qkv_pack", "direct", DIRECT_THREADS * 3 * -(-w.s_local * w.H * w.D // 8 // DIRECT_TILE))] = (
