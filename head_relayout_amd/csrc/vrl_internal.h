@@ -11,22 +11,31 @@ namespace vrl {
 // Workgroup shapes.  The direct and head-run kernels move one tile per
 // workgroup, each lane issuing its loads before its stores; the staged
 // kernel moves its LDS tile in batches of kStagedBatch vectors.  The direct
-// kernel runs one wave per workgroup with one vector per lane: 1 KiB tiles,
-// dispatched in address order, each workgroup's slot refilled as soon as its
-// one wave is done.  The head-run kernel takes 128 lanes with two vectors
-// each (16 tokens of a 128-element head per tile); the LDS transpose needs
-// its 256 lanes to fill and drain a tile.
+// kernel runs one wave per workgroup on 1 KiB tiles (one 16-byte vector per
+// lane): tiles dispatched in address order, each workgroup's slot refilled
+// as soon as its one wave is done.  The head-run
+// kernel takes 128 lanes on 4 KiB tiles (16 tokens of a 128-element head at
+// 16-byte vectors); the LDS transpose needs its 256 lanes to fill and drain
+// a tile.  Tile sizes are in bytes, so narrow vectors keep the same tiles.
 constexpr int kDirectThreads = 64;
-constexpr int kDirectUnroll = 1;
-constexpr uint32_t kDirectTile = uint32_t(kDirectThreads) * uint32_t(kDirectUnroll);
+constexpr uint32_t kDirectTileBytes = 1024;
+// Narrower vectors (operands not 16-byte aligned) move less per wave
+// instruction and do better with 256 lanes on 4 KiB tiles.
+constexpr int kNarrowThreads = 256;
+constexpr uint32_t kNarrowTileBytes = 4096;
 constexpr int kHeadrunThreads = 128;
-constexpr int kHeadrunUnroll = 2;
-constexpr uint32_t kHeadrunTile = uint32_t(kHeadrunThreads) * uint32_t(kHeadrunUnroll);
+constexpr uint32_t kHeadrunTileBytes = 4096;
 constexpr int kStagedThreads = 256;
 constexpr int kStagedUnroll = 8;
 constexpr uint32_t kStagedBatch = uint32_t(kStagedThreads) * uint32_t(kStagedUnroll);
-// Bound on any tile or batch, for the planner's index-range checks.
-constexpr uint32_t kMaxTileVecs = kStagedBatch;
+// Lanes and vectors per tile of the direct kernel at a vector width of vb
+// bytes; vectors per tile of the head-run kernel.
+constexpr int direct_threads(int vb) { return vb == 16 ? kDirectThreads : kNarrowThreads; }
+constexpr uint32_t direct_tile_vecs(int vb) { return (vb == 16 ? kDirectTileBytes : kNarrowTileBytes) / uint32_t(vb); }
+constexpr uint32_t headrun_tile_vecs(int vb) { return kHeadrunTileBytes / uint32_t(vb); }
+// Bound on any tile or batch in vectors (2-byte vectors), for the planner's
+// index-range checks.
+constexpr uint32_t kMaxTileVecs = kStagedBatch > kHeadrunTileBytes / 2 ? kStagedBatch : kHeadrunTileBytes / 2;
 
 // Head-major views (a head's tokens closer together than a token's heads)
 // whose head rows (2*D bytes) are narrower than this go through the LDS

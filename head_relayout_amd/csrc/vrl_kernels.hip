@@ -19,7 +19,7 @@
 // NaN payloads are preserved.
 //
 // Mapping to CDNA4.  One workgroup of the direct kernel -- a single wave64
-// -- moves one tile of kDirectTile consecutive vectors of one wire block;
+// -- moves one 1 KiB tile of consecutive vectors of one wire block;
 // the grid is flattened over (rank, chunk, plane, token tile).  Lanes take
 // consecutive 16-byte vectors, so the wave moves 1 KiB per instruction: four
 // 128-element head rows, contiguous on the wire side and, for
@@ -217,19 +217,22 @@ __device__ __forceinline__ Block locate(const KernelArgs &a)
     return b;
 }
 
-// Direct kernel: each workgroup moves kDirectTile consecutive vectors of a
-// wire block; the view side follows.  Used for every call except scatters
-// into head-major views.
+// Direct kernel: each workgroup moves one 1 KiB tile (kTile consecutive
+// vectors) of a wire block; the view side follows.  Used for every call
+// except scatters into head-major views.
 template <Op OP, int VB, bool CONTIG>
-__global__ __launch_bounds__(kDirectThreads) void relayout_kernel(const KernelArgs a)
+__global__ __launch_bounds__(direct_threads(VB)) void relayout_kernel(const KernelArgs a)
 {
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
     constexpr int VE = VB / 2;  // BF16 elements per vector
+    constexpr int kLanes = direct_threads(VB);
+    constexpr uint32_t kTile = direct_tile_vecs(VB);
+    constexpr int kU = int(kTile) / kLanes;  // vectors per lane
 
     const Block b = locate<OP>(a);
     const uint32_t nvec = uint32_t(b.T) * a.row_vecs;
-    const uint32_t f0 = b.tile * kDirectTile;
+    const uint32_t f0 = b.tile * kTile;
     if (f0 >= nvec)
         return;
     const int64_t st = b.st, sh = b.sh;
@@ -256,19 +259,19 @@ __global__ __launch_bounds__(kDirectThreads) void relayout_kernel(const KernelAr
     };
 
     const uint32_t f_lane = f0 + threadIdx.x;
-    if (f0 + kDirectTile <= nvec) {
+    if (f0 + kTile <= nvec) {
         // Full tile: all loads in flight before the first store.
-        V buf[kDirectUnroll];
+        V buf[kU];
 #pragma unroll
-        for (int u = 0; u < kDirectUnroll; ++u)
-            buf[u] = load_vec(src_of(f_lane + uint32_t(u * kDirectThreads)));
+        for (int u = 0; u < kU; ++u)
+            buf[u] = load_vec(src_of(f_lane + uint32_t(u * kLanes)));
 #pragma unroll
-        for (int u = 0; u < kDirectUnroll; ++u)
-            store_vec(dst_of(f_lane + uint32_t(u * kDirectThreads)), buf[u]);
+        for (int u = 0; u < kU; ++u)
+            store_vec(dst_of(f_lane + uint32_t(u * kLanes)), buf[u]);
     } else {
         // Last, partial tile of a block.
-        for (int u = 0; u < kDirectUnroll; ++u) {
-            const uint32_t f = f_lane + uint32_t(u * kDirectThreads);
+        for (int u = 0; u < kU; ++u) {
+            const uint32_t f = f_lane + uint32_t(u * kLanes);
             if (f < nvec)
                 store_vec(dst_of(f), load_vec(src_of(f)));
         }
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
 }
 
 // Head-run kernel, for views stored head-major: a workgroup moves TT
-// consecutive tokens of one head of a wire block (TT * head_vecs <= kHeadrunTile
+// consecutive tokens of one head of a wire block (TT * head_vecs <= headrun_tile_vecs(VB)
 // vectors), and consecutive workgroups take consecutive token tiles of the
 // same head.  The head-major side then sees one contiguous run per
 // workgroup and the chip writes (or reads) few runs at a time; the wire side
@@ -446,6 +449,8 @@ __global__ __launch_bounds__(kHeadrunThreads) void headrun_kernel(const KernelAr
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
     constexpr int VE = VB / 2;
+    constexpr uint32_t kTile = headrun_tile_vecs(VB);
+    constexpr int kU = int(kTile) / kHeadrunThreads;  // vectors per lane
 
     // token tile fastest, then what continues the same head's run
     const uint32_t tt_i = blockIdx.x % a.tok_tiles;
@@ -475,16 +480,16 @@ __global__ __launch_bounds__(kHeadrunThreads) void headrun_kernel(const KernelAr
         return reinterpret_cast<V *>(Tr::gather ? wire + off(i, row) : view + off(i, st));
     };
 
-    if (nv == kHeadrunTile) {
-        V buf[kHeadrunUnroll];
+    if (nv == kTile) {
+        V buf[kU];
 #pragma unroll
-        for (int u = 0; u < kHeadrunUnroll; ++u)
+        for (int u = 0; u < kU; ++u)
             buf[u] = load_vec(src_of(threadIdx.x + uint32_t(u * kHeadrunThreads)));
 #pragma unroll
-        for (int u = 0; u < kHeadrunUnroll; ++u)
+        for (int u = 0; u < kU; ++u)
             store_vec(dst_of(threadIdx.x + uint32_t(u * kHeadrunThreads)), buf[u]);
     } else {
-        for (int u = 0; u < kHeadrunUnroll; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const uint32_t i = threadIdx.x + uint32_t(u * kHeadrunThreads);
             if (i < nv)
                 store_vec(dst_of(i), load_vec(src_of(i)));
@@ -505,7 +510,7 @@ hipError_t launch_vb(const LaunchPlan &pl, hipStream_t stream)
                                dim3(kStagedThreads), kargs, pl.lds_bytes, stream);
     const void *fn = pl.contig ? reinterpret_cast<const void *>(&relayout_kernel<OP, VB, true>)
                                : reinterpret_cast<const void *>(&relayout_kernel<OP, VB, false>);
-    return hipLaunchKernel(fn, dim3(pl.grid), dim3(kDirectThreads), kargs, 0, stream);
+    return hipLaunchKernel(fn, dim3(pl.grid), dim3(direct_threads(VB)), kargs, 0, stream);
 }
 
 template <Op OP>

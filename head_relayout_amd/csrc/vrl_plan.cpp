@@ -98,14 +98,15 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     a.head_vecs = uint32_t(d->D / ve);
     magic_for(a.row_vecs, a.row_magic, a.row_shift);
     magic_for(a.head_vecs, a.head_magic, a.head_shift);
-    a.tiles = uint32_t((nvec_max + kDirectTile - 1) / kDirectTile);
+    const uint32_t dtile = direct_tile_vecs(vb), htile = headrun_tile_vecs(vb);
+    a.tiles = uint32_t((nvec_max + dtile - 1) / dtile);
 
     // A view whose heads lie further apart than its tokens (head-major
     // storage) makes the token and head axes swap for real: in wire order a
     // workgroup's writes into it scatter 2*D-byte pieces over all Gb heads,
     // and the chip has every head's stream open at once.  Scatters into such
     // views run as head runs instead: a workgroup moves TT consecutive
-    // tokens of one head (TT * head_vecs <= kHeadrunTile), consecutive
+    // tokens of one head (TT * head_vecs <= the head-run tile), consecutive
     // workgroups continue the same head.  Head rows narrower than a cache
     // line would make those runs read partial lines on the wire side, and
     // make wire-order gathers read partial lines of the view; such views go
@@ -152,8 +153,8 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
             ++a.swz_shift;
         pl.lds_bytes = uint32_t(tt * lrow_bytes);
         tiles = (Gb / gt) * int64_t(a.tok_tiles);
-    } else if (!gather && a.head_vecs <= kHeadrunTile) {
-        const int64_t tt = std::min<int64_t>(kHeadrunTile / a.head_vecs, t_max);
+    } else if (!gather && a.head_vecs <= htile) {
+        const int64_t tt = std::min<int64_t>(htile / a.head_vecs, t_max);
         pl.headrun = true;
         a.tile_tokens = uint32_t(tt);
         a.tok_tiles = uint32_t((t_max + tt - 1) / tt);

@@ -119,8 +119,10 @@ int main()
         {"unpack into head-major, D=8, 5 heads", Op::Unpack, 2, 4, 64, 10, 8, 0, true, 0, STAGED, 0, 5, 0, 16},
         {"unpack into head-major, one head per group", Op::Unpack, 2, 4, 64, 2, 128, 0, true, 0, DIRECT, 0, 0, 0, 16},
         {"unpack into head-major, D=16392", Op::Unpack, 2, 2, 3, 4, 16392, 0, true, 0, DIRECT, 0, 0, 0, 16},
-        {"unpack, views 2-byte aligned", Op::Unpack, 2, 4, 64, 8, 128, 0, false, 2, DIRECT, 0, 0, 0, 2},
-        {"unpack, views 8-byte aligned", Op::Unpack, 2, 4, 64, 8, 128, 0, false, 8, DIRECT, 0, 0, 0, 8},
+        // narrow vectors: 4 KiB tiles at every width: 16 tokens x 1 KiB rows -> 4 tiles per block
+        {"unpack, views 2-byte aligned", Op::Unpack, 2, 4, 64, 8, 128, 0, false, 2, DIRECT, 0, 0, 96, 2},
+        {"unpack, views 8-byte aligned", Op::Unpack, 2, 4, 64, 8, 128, 0, false, 8, DIRECT, 0, 0, 96, 8},
+        {"unpack into head-major, 4-byte aligned, D=128", Op::Unpack, 2, 4, 64, 8, 128, 0, true, 4, HEADRUN, 16, 0, 0, 4},
     };
     int bad = 0;
     for (const Case &k : cases)
