@@ -1245,8 +1245,9 @@ def whole_tensor_grids():
     w = datagen.WORKLOADS[3]
     out[("qkv_pack", "direct", DIRECT_THREADS * 3 * -(-w.s_local * w.H * w.D // 8 // DIRECT_TILE))] = (
         " (copy ceiling: P=1, C=1)", op_bytes(w)["qkv_pack"])
-    # the narrow-head workloads (LDS transpose: tiles of Gt heads filling a
-    # 128-byte line x as many tokens as fit 16 KiB, rounded to whole lines)
+    # the narrow-head workloads (LDS transpose: a scatter's tiles of Gt heads
+    # filling a 128-byte line x as many tokens as fit 8 KiB, a gather's of
+    # the whole group x as many as fit 16 KiB, rounded to whole lines)
     base = datagen.WORKLOADS[3]
     for D in (16, 32):
         s_local = base.s_local * base.D // D
@@ -1256,7 +1257,7 @@ def whole_tensor_grids():
         for op in ("qkv_unpack", "attn_split", "head_merge"):
             # a gather's tiles hold the whole group, a scatter's a line's worth of heads
             gt = G if op == "attn_split" else next(g for g in range(1, G + 1) if G % g == 0 and g * D * 2 >= 128)
-            tt = 16384 // (gt * hv * 16)
+            tt = (16384 if op == "attn_split" else 8192) // (gt * hv * 16)
             tt = min(tt - tt % quantum, t_max)
             blocks = base.P * base.C * (3 if op == "qkv_unpack" else 1)
             nbytes = op_bytes(base)[op]

@@ -10,13 +10,13 @@ namespace vrl {
 
 // Workgroup shapes.  The direct and head-run kernels move one tile per
 // workgroup, each lane issuing its loads before its stores; the staged
-// kernel moves its LDS tile in batches of kStagedBatch vectors.  The direct
-// kernel runs one wave per workgroup on 1 KiB tiles (one 16-byte vector per
-// lane): tiles dispatched in address order, each workgroup's slot refilled
-// as soon as its one wave is done.  The head-run
-// kernel takes 128 lanes on 4 KiB tiles (16 tokens of a 128-element head at
-// 16-byte vectors); the LDS transpose needs its 256 lanes to fill and drain
-// a tile.  Tile sizes are in bytes, so narrow vectors keep the same tiles.
+// kernel moves its LDS tile in batches.  The direct kernel runs one wave per
+// workgroup on 1 KiB tiles (one 16-byte vector per lane): tiles dispatched
+// in address order, each workgroup's slot refilled as soon as its one wave
+// is done.  The head-run kernel takes 128 lanes on 4 KiB tiles (16 tokens of
+// a 128-element head at 16-byte vectors); the LDS transpose needs its 256
+// lanes to fill and drain a tile.  Tile sizes are in bytes, so narrow
+// vectors keep the same tiles.
 constexpr int kDirectThreads = 64;
 constexpr uint32_t kDirectTileBytes = 1024;
 // Narrower vectors (operands not 16-byte aligned) move less per wave
@@ -26,8 +26,14 @@ constexpr uint32_t kNarrowTileBytes = 4096;
 constexpr int kHeadrunThreads = 128;
 constexpr uint32_t kHeadrunTileBytes = 4096;
 constexpr int kStagedThreads = 256;
-constexpr int kStagedUnroll = 8;
-constexpr uint32_t kStagedBatch = uint32_t(kStagedThreads) * uint32_t(kStagedUnroll);
+// The staged kernel's LDS tile and batch (vectors per lane per pass): 8 KiB
+// tiles moved 512 vectors at a time for scatters, 16 KiB tiles of whole wire
+// rows moved 2,048 at a time for gathers.
+constexpr uint32_t kScatterLdsBytes = 8192;
+constexpr int kScatterUnroll = 2;
+constexpr uint32_t kGatherLdsBytes = 16384;
+constexpr int kGatherUnroll = 8;
+constexpr uint32_t kStagedBatch = uint32_t(kStagedThreads) * uint32_t(kGatherUnroll);  // the larger batch
 // Lanes and vectors per tile of the direct kernel at a vector width of vb
 // bytes; vectors per tile of the head-run kernel.
 constexpr int direct_threads(int vb) { return vb == 16 ? kDirectThreads : kNarrowThreads; }
@@ -42,9 +48,6 @@ constexpr uint32_t kMaxTileVecs = kStagedBatch > kHeadrunTileBytes / 2 ? kStaged
 // transpose (staged_kernel); scatters into head-major views with wider head
 // rows run as head runs (headrun_kernel), gathers from them in wire order.
 constexpr int64_t kHeadrunMinBytes = 128;
-// LDS budget of one workgroup of the staged kernel; a tile holds as many
-// tokens of its Gt heads as fit.
-constexpr uint32_t kLdsBytes = 16384;
 
 enum class Op : int { Pack = 0, Unpack = 1, Split = 2, Merge = 3 };
 

@@ -348,6 +348,8 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
     using Tr = Traits<OP>;
     using V = typename Vec<VB>::type;
     constexpr int VE = VB / 2;
+    constexpr int kU = Tr::gather ? kGatherUnroll : kScatterUnroll;  // vectors per lane per pass
+    constexpr uint32_t kBatch = uint32_t(kStagedThreads) * uint32_t(kU);
     extern __shared__ __align__(16) unsigned char lds_raw[];
     V *const lds = reinterpret_cast<V *>(lds_raw);
 
@@ -396,12 +398,12 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
     };
 
     // Phase 1: source -> LDS, in the source's contiguous order.
-    for (uint32_t i0 = 0; i0 < nv; i0 += kStagedBatch) {
-        V buf[kStagedUnroll];
-        uint32_t slot[kStagedUnroll];
-        bool ok[kStagedUnroll];
+    for (uint32_t i0 = 0; i0 < nv; i0 += kBatch) {
+        V buf[kU];
+        uint32_t slot[kU];
+        bool ok[kU];
 #pragma unroll
-        for (int u = 0; u < kStagedUnroll; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const uint32_t i = i0 + uint32_t(u * kStagedThreads) + threadIdx.x;
             const Pos q = Tr::gather ? view_order(i < nv ? i : 0) : wire_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
@@ -410,19 +412,19 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
                 buf[u] = load_vec(reinterpret_cast<const V *>((Tr::gather ? view : wire) + q.off));
         }
 #pragma unroll
-        for (int u = 0; u < kStagedUnroll; ++u)
+        for (int u = 0; u < kU; ++u)
             if (ok[u])
                 lds[slot[u]] = buf[u];
     }
     __syncthreads();
     // Phase 2: LDS -> destination, in the destination's contiguous order (all
     // LDS reads of a batch first, then the stores).
-    for (uint32_t i0 = 0; i0 < nv; i0 += kStagedBatch) {
-        V buf[kStagedUnroll];
-        int64_t doff[kStagedUnroll];
-        bool ok[kStagedUnroll];
+    for (uint32_t i0 = 0; i0 < nv; i0 += kBatch) {
+        V buf[kU];
+        int64_t doff[kU];
+        bool ok[kU];
 #pragma unroll
-        for (int u = 0; u < kStagedUnroll; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const uint32_t i = i0 + uint32_t(u * kStagedThreads) + threadIdx.x;
             const Pos q = Tr::gather ? wire_order(i < nv ? i : 0) : view_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
                 buf[u] = lds[q.lds];
         }
 #pragma unroll
-        for (int u = 0; u < kStagedUnroll; ++u)
+        for (int u = 0; u < kU; ++u)
             if (ok[u])
                 store_vec(reinterpret_cast<V *>((Tr::gather ? wire : view) + doff[u]), buf[u]);
     }

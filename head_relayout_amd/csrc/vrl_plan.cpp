@@ -122,7 +122,8 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
     // heads per LDS-transpose tile: a gather writes whole wire rows (all Gb
     // heads, one write stream), a scatter the fewest heads that fill a line
     const int64_t gt = gather ? Gb : staged_heads(Gb, d->D);
-    const bool narrow = d->D * 2 < kHeadrunMinBytes && gt * a.head_vecs * vb <= int64_t(kLdsBytes);
+    const int64_t lds_budget = gather ? kGatherLdsBytes : kScatterLdsBytes;
+    const bool narrow = d->D * 2 < kHeadrunMinBytes && gt * a.head_vecs * vb <= lds_budget;
     int64_t tiles = a.tiles;
     if (!head_major || Gb <= 1) {
         // token-major (or one head per row): wire order (direct kernel)
@@ -130,7 +131,7 @@ bool plan_launch(Op op, const Problem &pb, const PlanView *views, int nviews, ui
         const int64_t lrow_bytes = gt * a.head_vecs * vb;
         // tokens per tile: as many as fit, rounded to whole lines of a head's run
         const int64_t quantum = std::max<int64_t>(1, 128 / (d->D * 2));
-        int64_t tt = int64_t(kLdsBytes) / lrow_bytes;
+        int64_t tt = lds_budget / lrow_bytes;
         if (tt >= quantum)
             tt -= tt % quantum;
         tt = std::min<int64_t>(tt, t_max);

@@ -109,7 +109,7 @@ hipError_t launch(const LaunchPlan &pl, hipStream_t)
     ++g_launches;
     if (pl.grid < 1 || pl.grid >= (uint32_t(1) << 31) ||
         !(pl.vec_bytes == 2 || pl.vec_bytes == 4 || pl.vec_bytes == 8 || pl.vec_bytes == 16) ||
-        pl.lds_bytes > kLdsBytes || pl.args.tiles < 1)
+        pl.lds_bytes > kGatherLdsBytes || pl.args.tiles < 1)
         g_launch_bad = true;
     return hipSuccess;
 }

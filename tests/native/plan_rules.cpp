@@ -5,8 +5,8 @@
 //
 // The rule: token-major views take the direct kernel; head-major views with
 // head rows narrower than a 128-byte line take the LDS transpose (for a
-// scatter Gt heads filling a line, for a gather the whole group, x as many
-// tokens as fit 16 KiB);
+// scatter Gt heads filling a line x as many tokens as fit 8 KiB, for a
+// gather the whole group x as many tokens as fit 16 KiB);
 // scatters into head-major views with wider rows take head runs (16 tokens
 // of one head per workgroup at head_dim 128), gathers from them the direct
 // kernel; so does any view whose head row is longer than one tile or whose
@@ -75,7 +75,9 @@ bool run(const Case &k)
         ok = ok && pl.grid == uint32_t(k.grid);
     if (got == STAGED) {  // the LDS tile fits the budget and holds whole rows
         const uint32_t gv = pl.args.group_heads * pl.args.head_vecs;
-        ok = ok && pl.lds_bytes <= kLdsBytes && pl.lds_bytes == pl.args.tile_tokens * gv * uint32_t(pl.vec_bytes);
+        const bool gather = k.op == Op::Pack || k.op == Op::Split;
+        ok = ok && pl.lds_bytes <= (gather ? kGatherLdsBytes : kScatterLdsBytes) &&
+             pl.lds_bytes == pl.args.tile_tokens * gv * uint32_t(pl.vec_bytes);
         // the column swizzle is a power-of-two mask dividing the row, so it
         // permutes columns within the row
         const uint32_t m = pl.args.swz_mask;
@@ -108,10 +110,10 @@ int main()
         {"unpack into head-major, D=64", Op::Unpack, 2, 4, 2 * R, 56, 64, 0, true, 0, HEADRUN, 32, 0, 0, 16},
         // 126-byte head rows: 2 heads fill a line; 2*63 2-byte vectors per LDS row
         {"unpack into head-major, D=63", Op::Unpack, 2, 3, 20, 4, 63, 0, true, 0, STAGED, 7, 2, 0, 2},
-        // 4 heads x 32 B fill a line; 8 vectors per LDS row -> 128 tokens
-        {"unpack into head-major, D=16", Op::Unpack, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 128, 4, 0, 16},
-        {"merge into head-major, D=16", Op::Merge, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 128, 4, 0, 16},
-        {"unpack into head-major, D=32", Op::Unpack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 128, 2, 0, 16},
+        // 4 heads x 32 B fill a line; 8 vectors per LDS row, 8 KiB scatter tiles -> 64 tokens
+        {"unpack into head-major, D=16", Op::Unpack, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 64, 4, 0, 16},
+        {"merge into head-major, D=16", Op::Merge, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 64, 4, 0, 16},
+        {"unpack into head-major, D=32", Op::Unpack, 2, 4, 4 * R, 56, 32, 0, true, 0, STAGED, 64, 2, 0, 16},
         // gathers: whole wire rows (28 heads); 56 vectors per LDS row -> 18 tokens, rounded to 16
         {"split from head-major, D=16", Op::Split, 2, 4, 8 * R, 56, 16, 0, true, 0, STAGED, 16, 28, 0, 16},
         // 112 vectors per LDS row -> 9 tokens, rounded to 8
