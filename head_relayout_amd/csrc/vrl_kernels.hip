@@ -397,7 +397,12 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
         return Pos{t, slot(t, h * hv + e), int64_t(t) * st + int64_t(h) * sh + int64_t(e) * VE};
     };
 
-    // Phase 1: source -> LDS, in the source's contiguous order.
+    // Phase 1: source -> LDS, in the source's contiguous order.  A scatter
+    // loads on every lane, a lane past the tile's end from the tile's first
+    // element (which always exists), so that no branch separates its loads:
+    // under per-vector branches the compiler waited for the first load
+    // before issuing the second.  A gather keeps the branches; its batch is
+    // larger than its tile, and the lanes past the tile skip their loads.
     for (uint32_t i0 = 0; i0 < nv; i0 += kBatch) {
         V buf[kU];
         uint32_t slot[kU];
@@ -408,8 +413,12 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
             const Pos q = Tr::gather ? view_order(i < nv ? i : 0) : wire_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
             slot[u] = q.lds;
-            if (ok[u])
-                buf[u] = load_vec(reinterpret_cast<const V *>((Tr::gather ? view : wire) + q.off));
+            if constexpr (Tr::gather) {
+                if (ok[u])
+                    buf[u] = load_vec(reinterpret_cast<const V *>(view + q.off));
+            } else {
+                buf[u] = load_vec(reinterpret_cast<const V *>(wire + (ok[u] ? q.off : 0)));
+            }
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
@@ -418,7 +427,8 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
     }
     __syncthreads();
     // Phase 2: LDS -> destination, in the destination's contiguous order (all
-    // LDS reads of a batch first, then the stores).
+    // LDS reads of a batch first, slot 0 standing in past the tile's end,
+    // then the stores, which alone are conditional).
     for (uint32_t i0 = 0; i0 < nv; i0 += kBatch) {
         V buf[kU];
         int64_t doff[kU];
@@ -429,8 +439,7 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
             const Pos q = Tr::gather ? wire_order(i < nv ? i : 0) : view_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
             doff[u] = q.off;
-            if (ok[u])
-                buf[u] = lds[q.lds];
+            buf[u] = lds[ok[u] ? q.lds : 0u];
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
