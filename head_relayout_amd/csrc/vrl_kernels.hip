@@ -401,8 +401,9 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
     // loads on every lane, a lane past the tile's end from the tile's first
     // element (which always exists), so that no branch separates its loads:
     // under per-vector branches the compiler waited for the first load
-    // before issuing the second.  A gather keeps the branches; its batch is
-    // larger than its tile, and the lanes past the tile skip their loads.
+    // before issuing the second.  A gather keeps the branches: its batch is
+    // larger than its tile at 16-byte vectors, and the lanes past the tile
+    // skip their loads and LDS reads.
     for (uint32_t i0 = 0; i0 < nv; i0 += kBatch) {
         V buf[kU];
         uint32_t slot[kU];
@@ -427,8 +428,8 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
     }
     __syncthreads();
     // Phase 2: LDS -> destination, in the destination's contiguous order (all
-    // LDS reads of a batch first, slot 0 standing in past the tile's end,
-    // then the stores, which alone are conditional).
+    // LDS reads of a batch first, then the stores; as in phase 1 a scatter
+    // reads on every lane, slot 0 standing in past the tile's end).
     for (uint32_t i0 = 0; i0 < nv; i0 += kBatch) {
         V buf[kU];
         int64_t doff[kU];
@@ -439,7 +440,12 @@ __global__ __launch_bounds__(kStagedThreads) void staged_kernel(const KernelArgs
             const Pos q = Tr::gather ? wire_order(i < nv ? i : 0) : view_order(i < nv ? i : 0);
             ok[u] = i < nv && q.t < tte;
             doff[u] = q.off;
-            buf[u] = lds[ok[u] ? q.lds : 0u];
+            if constexpr (Tr::gather) {
+                if (ok[u])
+                    buf[u] = lds[q.lds];
+            } else {
+                buf[u] = lds[ok[u] ? q.lds : 0u];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
