@@ -141,11 +141,6 @@ def fused_source(w: Workload, rank: int, out: np.ndarray | None = None) -> np.nd
     return out
 
 
-def qkv_column(w: Workload, which: int) -> int:
-    """First column of Q (0), K (1) or V (2) inside a fused row."""
-    return which * w.H * w.D
-
-
 def attention_output(w: Workload, rank: int, out: np.ndarray | None = None) -> np.ndarray:
     """A standalone per-rank attention output, uint16 [S][G][D] (stream 100 + rank).
 

@@ -26,10 +26,6 @@ def dev_qkv(fused: torch.Tensor, H: int, D: int):
     return [fused[:, i * H * D:(i + 1) * H * D].unflatten(1, (H, D)) for i in range(3)]
 
 
-def _host_like(view: torch.Tensor) -> np.ndarray:
-    return np.zeros(tuple(view.shape), dtype=np.uint16)
-
-
 def run_pipeline(dev, P, C, S_l, H, D, fused, tag, planes=(0, 1, 2), unpack_layout=None,
                  merge_layout=None, base_offset=0, chunk_heads=False):
     """fused: per-rank host uint16 [S_l][3*H*D + pad] sources.
