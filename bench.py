@@ -391,6 +391,10 @@ def _queued(torch, fn, sets, reps):
 
 
 def _stats(ts, mean=None, nbytes=None) -> dict:
+    """Median, p10, p90 and count of sorted per-call times `ts` (ms), with the
+    queue mean and the rate for `nbytes` when given."""
+    if any(a > b for a, b in zip(ts, ts[1:])):
+        raise ValueError("_stats needs sorted times")
     n = len(ts)
     out = {"ms_median": round(ts[n // 2], 5), "ms_p10": round(ts[n // 10], 5),
            "ms_p90": round(ts[(9 * n) // 10], 5), "launches": n}
@@ -461,14 +465,11 @@ def reference_arm(torch, vrl, w, ranks, reps=16):
             if not torch.equal(x.reshape(-1).view(torch.int16), y.reshape(-1).view(torch.int16)):
                 raise SystemExit(f"reference and direct {name} differ")
         del a, b
-        for fn in (ref_fn, dir_fn):      # warm-up: each set once
-            for x in sets:
-                fn(x)
         ra, ra_mean = _queued(torch, ref_fn, sets, reps)
         dm, dm_mean = _queued(torch, dir_fn, sets, reps)
         rb, rb_mean = _queued(torch, ref_fn, sets, reps)
         ref_med = (ra[len(ra) // 2] + rb[len(rb) // 2]) / 2
-        entry = {"reference": _stats(ra + rb, (ra_mean + rb_mean) / 2), "direct": _stats(dm, dm_mean),
+        entry = {"reference": _stats(sorted(ra + rb), (ra_mean + rb_mean) / 2), "direct": _stats(dm, dm_mean),
                  "reference_ms": round(ref_med, 5), "direct_ms": round(dm[len(dm) // 2], 5),
                  "speedup": round(ref_med / dm[len(dm) // 2], 3), "bytes": nbytes, "buffer_sets": k}
         if name == "attn_split_one_chunk":

@@ -109,3 +109,19 @@ def test_trace_summary_labels_workloads_and_windows(tmp_path, capsys):
     win = [l for l in out if l.startswith("direct qkv_pack (window)")]
     assert len(win) == 1 and win[0].split()[-2:] == ["-", "-"]
     assert any(l.startswith("__amd_rocclr_copyBuffer") for l in out)
+
+
+def test_stats_positions_and_sorted_input():
+    """_stats reads median, p10 and p90 by position, so it takes sorted times
+    only (the reference arm's two passes are merged and sorted first)."""
+    import bench
+
+    ts = [float(i) for i in range(1, 21)]            # 1 .. 20 ms
+    s = bench._stats(ts, mean=10.0, nbytes=8_000_000_000)
+    assert (s["ms_median"], s["ms_p10"], s["ms_p90"], s["launches"]) == (11.0, 3.0, 19.0, 20)
+    assert s["ms_mean_queued"] == 10.0
+    assert s["gbs"] == round(8e9 / 11e-3 / 1e9, 1)
+    a, b = ts[::2], ts[1::2]                         # two sorted passes
+    with pytest.raises(ValueError):
+        bench._stats(a + b)
+    assert bench._stats(sorted(a + b)) == bench._stats(ts)
