@@ -26,7 +26,7 @@ from tests.gpu_harness import SENTINEL, assert_bits_equal, assert_guard_intact, 
 pytestmark = pytest.mark.gpu
 
 # Case count and seed; the environment may ask for a longer or different sweep.
-N_CASES = int(os.environ.get("VRL_RANDOM_CASES", "2000"))
+N_CASES = int(os.environ.get("VRL_RANDOM_CASES", "5000"))
 SEED = int(os.environ.get("VRL_RANDOM_SEED", "20261202"))
 
 
