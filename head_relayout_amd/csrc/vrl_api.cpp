@@ -2,8 +2,8 @@
 //
 // Every check runs before anything is enqueued, in this order: dimensions and
 // window (VRL_E_INVALID), pointers and layouts (VRL_E_INVALID / VRL_E_LAYOUT),
-// the launch plan's size limits (VRL_E_INVALID, vrl_plan.cpp), then the device and the
-// pointers' allocations (VRL_E_DEVICE / VRL_E_INVALID).  All but the last
+// the launch plan's size limits (VRL_E_INVALID, vrl_plan.cpp), then the device, the
+// stream's device and the pointers' allocations (VRL_E_DEVICE / VRL_E_INVALID).  All but the last
 // group need no GPU, so they are exercised by the host-only tests.  The fail-closed behaviour (no silent fallback; layouts
 // outside the contract are reported so the caller keeps its materialising
 // path) follows the Vflash "Sol-Engine alignment" page, "What is enabled",
@@ -219,6 +219,23 @@ vrl_status check_device(int &dev)
     return VRL_OK;
 }
 
+// A stream other than the null stream must belong to `dev`: the memory
+// checks below are made against that device, and a kernel enqueued on
+// another device's stream would run there.
+vrl_status check_stream(void *stream, int dev)
+{
+    if (!stream)
+        return VRL_OK;
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(VRL_E_DEVICE, "cannot query the device of hip_stream");
+    }
+    if (sdev != dev)
+        return fail(VRL_E_DEVICE, "hip_stream belongs to device %d, not the current device %d", int(sdev), dev);
+    return VRL_OK;
+}
+
 // Each view must be device memory of `dev` and lie inside its allocation.
 vrl_status check_memory(const Geom *gs, int n, int dev)
 {
@@ -267,6 +284,8 @@ vrl_status run(vrl::Op op, const vrl_dims *d, const Geom *views, int nviews, con
         return fail(VRL_E_INVALID, "%s", why);
     int dev = 0;
     if ((s = check_device(dev)) != VRL_OK)
+        return s;
+    if ((s = check_stream(stream, dev)) != VRL_OK)
         return s;
     if ((s = check_memory(all, nviews + 1, dev)) != VRL_OK)
         return s;

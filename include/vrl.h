@@ -37,8 +37,9 @@
  * The library allocates no memory, keeps no pointer after a call returns and
  * holds no mutable global state besides a per-device architecture cache and
  * a per-thread error message, so calls are thread-safe.  Work is enqueued
- * asynchronously on `hip_stream` (a hipStream_t; NULL is the null stream);
- * buffers must stay alive until the stream has passed the work.
+ * asynchronously on `hip_stream` (a hipStream_t of the current device; NULL
+ * is the null stream); buffers must stay alive until the stream has passed
+ * the work.
  *
  * Windows.  Every relayout takes a chunk window [c_begin, c_end) with
  * 0 <= c_begin < c_end <= C; (0, C) is the whole tensor.  Only the window's
@@ -64,8 +65,9 @@
  *                  is not 2-byte aligned.  The caller keeps its reference
  *                  (materialising) path for such layouts; the library never
  *                  falls back silently.
- *   VRL_E_DEVICE   the current device is not gfx950, a pointer is not device
- *                  memory of the current device, or a HIP call failed.
+ *   VRL_E_DEVICE   the current device is not gfx950, `hip_stream` or a
+ *                  pointer belongs to another device, a pointer is not device
+ *                  memory, or a HIP call failed.
  * No C++ exception crosses this interface.
  */
 #ifndef VRL_H

@@ -91,6 +91,24 @@ hipError_t hipPointerGetAttributes(hipPointerAttribute_t *attr, const void *p)
     return hipSuccess;
 }
 
+// Fake streams: kStream0 belongs to device 0, kStream1 to device 1, any
+// other non-null handle is unknown.
+void *const kStream0 = reinterpret_cast<void *>(uintptr_t(0x5000));
+void *const kStream1 = reinterpret_cast<void *>(uintptr_t(0x5100));
+
+hipError_t hipStreamGetDevice(hipStream_t stream, hipDevice_t *device)
+{
+    if (reinterpret_cast<void *>(stream) == kStream0) {
+        *device = 0;
+        return hipSuccess;
+    }
+    if (reinterpret_cast<void *>(stream) == kStream1) {
+        *device = 1;
+        return hipSuccess;
+    }
+    return hipErrorInvalidHandle;
+}
+
 hipError_t hipMemGetAddressRange(hipDeviceptr_t *base, size_t *size, hipDeviceptr_t p)
 {
     const uintptr_t u = reinterpret_cast<uintptr_t>(p);
@@ -194,13 +212,13 @@ Args valid_args(int op, const vrl_dims &d)
     return a;
 }
 
-vrl_status call(int op, const vrl_dims *d, Args &a, int32_t cb, int32_t ce)
+vrl_status call(int op, const vrl_dims *d, Args &a, int32_t cb, int32_t ce, void *stream = nullptr)
 {
     switch (op) {
-    case 0: return vrl_qkv_pack(d, &a.v[0], &a.v[1], &a.v[2], a.wire, cb, ce, nullptr);
-    case 1: return vrl_qkv_unpack(d, a.wire, &a.v[0], &a.v[1], &a.v[2], cb, ce, nullptr);
-    case 2: return vrl_attn_split(d, &a.v[0], a.wire, cb, ce, nullptr);
-    default: return vrl_head_merge(d, a.wire, &a.v[0], cb, ce, nullptr);
+    case 0: return vrl_qkv_pack(d, &a.v[0], &a.v[1], &a.v[2], a.wire, cb, ce, stream);
+    case 1: return vrl_qkv_unpack(d, a.wire, &a.v[0], &a.v[1], &a.v[2], cb, ce, stream);
+    case 2: return vrl_attn_split(d, &a.v[0], a.wire, cb, ce, stream);
+    default: return vrl_head_merge(d, a.wire, &a.v[0], cb, ce, stream);
     }
 }
 
@@ -246,8 +264,14 @@ int main()
             cb = int32_t(below(7)) - 1;
             ce = int32_t(below(7)) - 1;
         }
+        // mostly the null stream; sometimes a stream of the current device, of
+        // another device, or an unknown handle
+        const uint64_t sk = below(16);
+        void *const stream = sk < 12 ? nullptr : sk < 14 ? kStream0 : sk < 15 ? kStream1
+                                                 : reinterpret_cast<void *>(uintptr_t(0x5200));
+        const bool stream_ok = stream == nullptr || stream == kStream0;
         const int before = g_launches;
-        const vrl_status s = call(op, &d, a, cb, ce);
+        const vrl_status s = call(op, &d, a, cb, ce, stream);
         const bool launched = g_launches != before;
         if (s == VRL_OK) {
             ++accepted;
@@ -255,6 +279,8 @@ int main()
                 report(it, "accepted without a launch", op, s);
             if (g_mode != GFX950 || g_foreign)
                 report(it, "accepted without a gfx950 owning the memory", op, s);
+            if (!stream_ok)
+                report(it, "accepted with another device's or an unknown stream", op, s);
         } else {
             if (launched)
                 report(it, "launched but reported an error", op, s);
@@ -266,8 +292,10 @@ int main()
         const bool window_ok = cb >= 0 && cb < ce && ce <= d.C;
         if (valid_layout && window_ok && g_mode == GFX950 && !g_foreign) {
             ++valid_calls;
-            if (s != VRL_OK)
+            if (stream_ok && s != VRL_OK)
                 report(it, "in-contract call rejected", op, s);
+            if (!stream_ok && s != VRL_E_DEVICE)
+                report(it, "stream of another device not refused as a device error", op, s);
         }
         // the sizing helpers: -1 exactly when a reason is recorded
         if ((vrl_exchange_elems(int(below(3)) - 1, &d) < 0) != (vrl_last_error()[0] != 0))
