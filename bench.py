@@ -322,6 +322,8 @@ def run_bench(args):
         result["overlap_link_model"] = overlap_schedule(torch, w, ranks, engine="link", kernels_ms=kernels_ms)
         say("[bench] head-chunked layout")
         result["head_chunks"] = head_chunk_layout(torch, vrl, w, ranks)
+        say("[bench] host cost of one call")
+        result["host_cost_us"] = host_cost(torch, vrl)
         say("[bench] head-major (BHTD) attention side")
         result["head_major"] = head_major_layouts(torch, vrl, w, ranks[0])
         if w.cid == 3:
@@ -718,6 +720,51 @@ def head_chunk_layout(torch, vrl, w, ranks):
     ts, mean = _queued(torch, lambda st: vrl.attn_split(st[0], st[1], P, C, 0, 1, **hc), sets, 24)
     out["attn_split_one_chunk"] = _stats(ts, mean, one)
     out["attn_split_one_chunk"]["output_bytes"] = S * (G // C) * D * 2
+    return out
+
+
+def host_cost(torch, vrl, calls=2000):
+    """Host time to enqueue one call, in microseconds: a one-chunk split of
+    a tiny attention output (two ranks of 64 tokens, 2 x 4 heads of 16), so
+    that the GPU stays ahead of the host and the launch queue never fills.
+    Through the C ABI by ctypes with the arguments built once (validation,
+    the device, stream and pointer-attribute queries and the launch), and
+    through the torch binding (which also builds the arguments from the
+    tensors).  No synchronisation inside the timed loops."""
+    import ctypes
+
+    from head_relayout_amd import _lib
+
+    P, C, S_l, H, D = 2, 4, 64, 8, 16
+    G, S = H // P, P * S_l
+    dev = torch.device("cuda:0")
+    o = torch.empty(S, G, D, dtype=torch.int16, device=dev).random_(-30000, 30000).view(torch.bfloat16)
+    send = torch.zeros(S * G * D, dtype=torch.bfloat16, device=dev)
+    lib = _lib.lib()
+    dims = _lib.Dims(P, C, S_l, H, D, 0)
+    view = _lib.View(o.data_ptr(), G * D, D)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def c_abi():
+        if lib.vrl_attn_split(ctypes.byref(dims), ctypes.byref(view), send.data_ptr(), 0, 1, stream) != 0:
+            raise SystemExit("host cost: the C-ABI call failed")
+
+    def binding():
+        vrl.attn_split(o, send, P, C, 0, 1)
+
+    out = {"calls": calls}
+    for name, fn in (("c_abi", c_abi), ("binding", binding)):
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        out[name] = round(1e6 * (t1 - t0) / calls, 2)
+    if not torch.equal(send.view(torch.int16)[:S_l // C * G * D], o.view(torch.int16).reshape(-1)[:S_l // C * G * D]):
+        raise SystemExit("host cost: the one-chunk split wrote the wrong bytes")
     return out
 
 

@@ -45,7 +45,8 @@ def test_bench_json_line(gpu):
 def test_bench_sections_mid_size(gpu):
     """Every section outside the timed step -- one-chunk windows, the copy
     ceiling, the overlap schedule with each stand-in exchange, head chunks,
-    head-major layouts and the reference arm -- at the mid-size workload.
+    the host cost of a call, head-major layouts and the reference arm -- at
+    the mid-size workload.
     Each section checks its own outputs (round trips, windows against the
     whole call, agreement with the direct or token-major results) and makes
     the run exit non-zero otherwise."""
@@ -55,9 +56,11 @@ def test_bench_sections_mid_size(gpu):
     assert r.returncode == 0, r.stderr[-2000:]
     d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
     for key in ("windows", "copy_ceiling", "overlap", "overlap_sdma", "overlap_link_model", "head_chunks",
-                "head_major", "reference_arm"):
+                "host_cost_us", "head_major", "reference_arm"):
         assert key in d, key
     assert 0 < d["copy_ceiling"]["pct_peak"] < 100
+    hc = d["host_cost_us"]
+    assert hc["calls"] == 2000 and 0 < hc["c_abi"] < hc["binding"] < 1000
     for op in ("qkv_pack", "qkv_unpack", "attn_split", "head_merge"):
         win = d["windows"][op]
         assert all(win[f"chunk_{c}"]["ms_median"] > 0 for c in range(4))
