@@ -969,17 +969,19 @@ def cpu_baseline(w, hosts, nbytes, reps=21, single_reps=3):
                      np.full(oracle.exchange_elems(d, 1), 0, dtype=np.uint16),
                      np.full((w.s_local, w.H, w.D), 0, dtype=np.uint16)))
 
+    peaks = {}
+
     def one_pass():
         t = {"qkv_pack": 0.0, "qkv_unpack": 0.0, "attn_split": 0.0, "head_merge": 0.0}
         for qkv, packed, planes, send, merged in bufs:
             t0 = time.perf_counter()
-            oracle.qkv_pack(d, *qkv, packed)
+            peaks["qkv_pack"] = oracle.qkv_pack(d, *qkv, packed)
             t1 = time.perf_counter()
-            oracle.qkv_unpack(d, packed, *planes)
+            peaks["qkv_unpack"] = oracle.qkv_unpack(d, packed, *planes)
             t2 = time.perf_counter()
-            oracle.attn_split(d, planes[0], send)
+            peaks["attn_split"] = oracle.attn_split(d, planes[0], send)
             t3 = time.perf_counter()
-            oracle.head_merge(d, send, merged)
+            peaks["head_merge"] = oracle.head_merge(d, send, merged)
             t4 = time.perf_counter()
             t["qkv_pack"] += t1 - t0
             t["qkv_unpack"] += t2 - t1
@@ -999,7 +1001,8 @@ def cpu_baseline(w, hosts, nbytes, reps=21, single_reps=3):
               "sample": f"one step of the workload (the pack, unpack, split and merge chains for each "
                         f"of the {len(hosts)} ranks, each rank's packed buffer standing in for its "
                         f"exchanged one); median of {reps} timed passes after one untimed pass",
-              "ms": {k: round(1e3 * v, 1) for k, v in med.items()}}
+              "ms": {k: round(1e3 * v, 1) for k, v in med.items()},
+              "materialised_peak_bytes": dict(peaks)}
     # the same chains on one thread, one rank
     say(f"[bench] cpu baseline: one thread, one rank, {single_reps} passes")
     del bufs[1:]

@@ -33,6 +33,11 @@ def test_cpu_baseline_on_the_tiny_workload():
     out = bench.cpu_baseline(w, hosts, bench.op_bytes(w), reps=3, single_reps=1)
     assert out["kind"] == "oracle" and out["unit"] == "GB/s" and out["value"] > 0
     assert out["cores"] >= 1
+    # the chains' peaks: twice the output for the pack and the merge, the
+    # factor of the page's allocation screen (24,576 and 8,192 B outputs here)
+    nb = bench.op_bytes(w)
+    assert out["materialised_peak_bytes"]["qkv_pack"] == nb["qkv_pack"] == 2 * 24576
+    assert out["materialised_peak_bytes"]["head_merge"] == nb["head_merge"] == 2 * 8192
     json.dumps(out)
 
 
