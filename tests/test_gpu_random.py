@@ -1,7 +1,8 @@
 """Seeded random parity sweep of all four relayouts against the oracle.
 
-Each case draws P, the head-group size (1-6, 8, 12 or 28 heads: the LDS
-transpose then tiles several heads of a group), head_dim, tokens per rank,
+Each case draws P (1-6, 8 or 16 ranks), the head-group size (1-6, 8, 12
+or 28 heads: the LDS transpose then tiles several heads of a group),
+head_dim, tokens per rank,
 the chunk reading (tokens or heads) and count, a chunk window, and the
 layouts of every operand: the pack's Q/K/V either as column blocks of fused
 projection rows (with padded rows) or each in a layout of its own, and the
@@ -73,7 +74,7 @@ def _dev_guarded(host, dev):
 
 def _case(rng, tokens=(1, 41), dims=(2, 4, 6, 8, 16, 24, 64, 128), max_elems=None):
     while True:
-        P = int(rng.choice([1, 2, 3, 4, 8]))
+        P = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16]))
         G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 28]))
         H = P * G
         D = int(rng.choice(dims))
