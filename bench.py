@@ -185,10 +185,10 @@ def run_bench(args):
     nbytes = op_bytes(w)
     step_bytes = P * sum(nbytes.values())
 
-    def step(events=None):
+    def step(events=None, only=None):
         for name, fn in ops:
             for rk in ranks:
-                if events is not None:
+                if events is not None and (only is None or name in only):
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record()
@@ -203,15 +203,29 @@ def run_bench(args):
         step()
     torch.cuda.synchronize()
 
-    say(f"[bench] timing {args.steps} steps")
+    # The timed region: HIP events only around the pack launches (the
+    # roofline kernel).  Every timing event costs the step about 4 us (the
+    # queue drains to stamp it), so events around all eight launches would
+    # slow the step by some 3 %; the per-op table comes from a second pass
+    # that has them.
+    say(f"[bench] timing {args.steps} steps (HIP events around the pack launches)")
+    pack_events = {name: [] for name, _ in ops}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(pack_events, only=("qkv_pack",))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    say(f"[bench] per-op pass: {args.steps} steps with HIP events around every launch")
     events = {name: [] for name, _ in ops}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(events)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / args.steps
+    ms_per_step_all_events = 1e3 * (time.perf_counter() - t0) / args.steps
 
     per_op = {}
     for name, _ in ops:
@@ -274,12 +288,14 @@ def run_bench(args):
         per_op[name]["pct_of_elementwise_copy"] = round(100 * med_gbs / elementwise[key]["gbs"], 1)
         per_op[name]["pct_of_copy_ceiling"] = round(100 * med_gbs / ceiling["gbs"], 1)
 
+    # the dominant kernel's mean launch duration, from the timed region's events
     dominant = "qkv_pack"
-    achieved = per_op[dominant]["gbs"]
+    dom_times = [a.elapsed_time(b) for a, b in pack_events[dominant]]
+    achieved = round(nbytes[dominant] / (sum(dom_times) / len(dom_times) * 1e-3) / 1e9, 1)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(),
                 "kernel": "qkv_pack (relayout_kernel<Pack, 16 B, contiguous>)",
-                "bytes_per_launch": nbytes[dominant]}
+                "bytes_per_launch": nbytes[dominant], "launches": len(dom_times)}
 
     result = {
         "metric": METRIC,
@@ -289,6 +305,7 @@ def run_bench(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_events_on_every_launch": round(ms_per_step_all_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
